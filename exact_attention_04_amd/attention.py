@@ -1,0 +1,111 @@
+"""Python entry point over the C ABI: argument marshalling only.
+
+``attention(q, k, v, causal=..., window_size=..., softmax_scale=...)`` mirrors
+the call the "Flash Attention | Hermes Skill" page shows for the flash-attn
+library (Workflow 2, Step 2: q, k, v as [batch, seqlen, nheads, headdim],
+``causal``, ``window_size=(left, right)`` with -1 for no limit,
+``softmax_scale=None`` for 1/sqrt(headdim)) and accepts the SDPA layout
+[batch, heads, seq, dim] of its Quick start with ``layout="bhsd"``.
+
+Every step of the computation runs in the HIP library; torch provides device
+memory (``torch.empty``), pointers, strides and the current stream.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+
+_DTYPES = {
+    torch.float16: _lib.EA_F16,
+    torch.bfloat16: _lib.EA_BF16,
+    torch.float8_e4m3fn: _lib.EA_FP8_E4M3,
+    torch.float32: _lib.EA_F32,
+}
+
+
+def _dims(x: torch.Tensor, layout: str):
+    """(B, S, H, D) and the element strides (b, s, h) of a 4-D tensor."""
+    if x.dim() != 4:
+        raise ValueError(f"expected a 4-D tensor, got shape {tuple(x.shape)}")
+    if x.stride(3) != 1 and x.shape[3] > 1:
+        raise ValueError("the head dimension must be contiguous (stride 1)")
+    st = x.stride()
+    if layout == "bshd":
+        return (x.shape[0], x.shape[1], x.shape[2], x.shape[3]), (st[0], st[1], st[2])
+    if layout == "bhsd":
+        return (x.shape[0], x.shape[2], x.shape[1], x.shape[3]), (st[0], st[2], st[1])
+    raise ValueError(f"layout must be 'bshd' or 'bhsd', got {layout!r}")
+
+
+def make_args(q, k, v, o, lse, *, causal=False, window_size=(-1, -1), softmax_scale=None,
+              layout="bshd", descale=None) -> _lib.AttnArgs:
+    """Fill an ``ea_attn_args`` for the given tensors (no checks beyond shapes)."""
+    (B, N, H, D), (qb, qs, qh) = _dims(q, layout)
+    (Bk, Nk, Hk, Dk), (kb, ks, kh) = _dims(k, layout)
+    (_, _, _, _), (vb, vs, vh) = _dims(v, layout)
+    (_, _, _, _), (ob, os_, oh) = _dims(o, layout)
+    if Bk != B or Dk != D or tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError(f"unsupported dtypes q={q.dtype} k={k.dtype} v={v.dtype}")
+    a = _lib.AttnArgs()
+    a.struct_size = _lib.ctypes.sizeof(_lib.AttnArgs)
+    a.in_dtype = _DTYPES[q.dtype]
+    a.out_dtype = _DTYPES.get(o.dtype, 0)
+    a.causal = 1 if causal else 0
+    a.window_left, a.window_right = int(window_size[0]), int(window_size[1])
+    a.softmax_scale = float(1.0 / math.sqrt(D) if softmax_scale is None else softmax_scale)
+    dq, dk, dv = (1.0, 1.0, 1.0) if descale is None else descale
+    a.q_descale, a.k_descale, a.v_descale = float(dq), float(dk), float(dv)
+    a.batch, a.seqlen_q, a.seqlen_k, a.nheads_q, a.nheads_k, a.headdim = B, N, Nk, H, Hk, D
+    a.q, a.k, a.v, a.o = q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr()
+    a.q_stride_b, a.q_stride_s, a.q_stride_h = qb, qs, qh
+    a.k_stride_b, a.k_stride_s, a.k_stride_h = kb, ks, kh
+    a.v_stride_b, a.v_stride_s, a.v_stride_h = vb, vs, vh
+    a.o_stride_b, a.o_stride_s, a.o_stride_h = ob, os_, oh
+    if lse is not None:
+        a.lse = lse.data_ptr()
+        a.lse_stride_b, a.lse_stride_h = lse.stride(0), lse.stride(1)
+    return a
+
+
+def out_dtype_for(dtype: torch.dtype) -> torch.dtype:
+    return torch.bfloat16 if dtype == torch.float8_e4m3fn else dtype
+
+
+def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = False,
+              window_size: Tuple[int, int] = (-1, -1), softmax_scale: Optional[float] = None,
+              layout: str = "bshd", descale: Optional[Tuple[float, float, float]] = None,
+              return_lse: bool = True, out: Optional[torch.Tensor] = None,
+              lse: Optional[torch.Tensor] = None):
+    """Exact attention forward on the current HIP stream.
+
+    Returns ``(o, lse)``: o in q's layout and shape (bf16 for fp8 inputs, else
+    q's dtype), lse as float32 [B, H, N] (None when ``return_lse`` is False).
+    ``descale`` gives the per-tensor fp8 scales (stored value * descale = real
+    value).  Raises ValueError for arguments the library rejects.
+    """
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor (this library has no CPU path)")
+    (B, N, H, _), _ = _dims(q, layout)
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype_for(q.dtype), device=q.device)
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if not return_lse:
+        lse = None
+    a = make_args(q, k, v, out, lse, causal=causal, window_size=window_size, softmax_scale=softmax_scale,
+                  layout=layout, descale=descale)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    _lib.check(_lib.fwd(a, stream))
+    return out, lse
+
+
+def plan(q, k, v, o, lse=None, **kw) -> _lib.PlanInfo:
+    """The tile configuration ``attention`` would launch (no device work)."""
+    return _lib.plan(make_args(q, k, v, o, lse, **kw))

@@ -1,0 +1,233 @@
+// C ABI of the exact-attention forward: argument checks, planning and launch.
+// The contract of every entry point is stated in include/ea_attn.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+
+#include "ea_attn.h"
+#include "fwd_kernel.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_dev_once[kMaxDevices];
+bool g_dev_is_gfx950[kMaxDevices];
+
+bool device_is_gfx950(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return false;
+  std::call_once(g_dev_once[dev], [dev] {
+    hipDeviceProp_t prop;
+    g_dev_is_gfx950[dev] = false;
+    if (hipGetDeviceProperties(&prop, dev) == hipSuccess) {
+      // gcnArchName looks like "gfx950:sramecc+:xnack-"
+      g_dev_is_gfx950[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 &&
+                             (prop.gcnArchName[6] == '\0' || prop.gcnArchName[6] == ':');
+    }
+  });
+  return g_dev_is_gfx950[dev];
+}
+
+int elem_bytes(int dtype) {
+  switch (dtype) {
+    case EA_F16:
+    case EA_BF16: return 2;
+    case EA_FP8_E4M3: return 1;
+    case EA_F32: return 4;
+    default: return 0;
+  }
+}
+
+// Byte range [lo, hi) spanned by a [B, S, H, D] strided tensor (strides >= 0).
+struct Span {
+  uintptr_t lo, hi;
+};
+Span span_of(const void* base, int64_t B, int64_t S, int64_t H, int64_t D, int64_t sb, int64_t ss, int64_t sh,
+             int esz) {
+  const int64_t last = (B - 1) * sb + (S - 1) * ss + (H - 1) * sh + D;
+  const uintptr_t lo = (uintptr_t)base;
+  return {lo, lo + (uintptr_t)(last * esz)};
+}
+bool overlaps(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Checks shared by ea_attn_fwd and ea_attn_plan.  Returns EA_OK, or the error.
+// Sets *empty when there is nothing to compute.
+int validate(const ea_attn_args* a, bool* empty) {
+  *empty = false;
+  if (a == nullptr || a->struct_size < sizeof(ea_attn_args)) return EA_EINVAL;
+  if (a->batch < 0 || a->seqlen_q < 0 || a->seqlen_k < 0 || a->nheads_q < 1 || a->nheads_k < 1 ||
+      a->headdim < 1)
+    return EA_EINVAL;
+  if (elem_bytes(a->in_dtype) == 0 || elem_bytes(a->out_dtype) == 0) return EA_EINVAL;
+  if (!std::isfinite(a->softmax_scale)) return EA_EINVAL;
+  const bool fp8 = a->in_dtype == EA_FP8_E4M3;
+  const float ds[3] = {a->q_descale, a->k_descale, a->v_descale};
+  for (float d : ds) {
+    if (!std::isfinite(d) || !(d > 0.f)) return EA_EINVAL;
+    if (!fp8 && d != 1.0f) return EA_EINVAL;
+  }
+  if (a->window_left < -1 || a->window_right < -1) return EA_EINVAL;
+
+  // what the kernels implement
+  if (a->in_dtype == EA_F32) return EA_EUNSUPPORTED;
+  if (fp8 ? a->out_dtype != EA_BF16 : a->out_dtype != a->in_dtype) return EA_EUNSUPPORTED;
+  if (a->headdim != 64 && a->headdim != 128) return EA_EUNSUPPORTED;
+  if (fp8 && a->headdim != 128) return EA_EUNSUPPORTED;
+  if (a->seqlen_q != a->seqlen_k) return EA_EUNSUPPORTED;
+  if (a->nheads_q != a->nheads_k) return EA_EUNSUPPORTED;
+  if (!(a->softmax_scale > 0.f)) return EA_EUNSUPPORTED;
+
+  if (a->batch == 0 || a->seqlen_q == 0) {
+    *empty = true;
+    return EA_OK;
+  }
+  if (a->q == nullptr || a->k == nullptr || a->v == nullptr || a->o == nullptr) return EA_EINVAL;
+
+  const int64_t B = a->batch, N = a->seqlen_q, H = a->nheads_q, D = a->headdim;
+  const int ein = elem_bytes(a->in_dtype), eout = elem_bytes(a->out_dtype);
+  const int64_t strides[12] = {a->q_stride_b, a->q_stride_s, a->q_stride_h, a->k_stride_b, a->k_stride_s, a->k_stride_h,
+                               a->v_stride_b, a->v_stride_s, a->v_stride_h, a->o_stride_b, a->o_stride_s, a->o_stride_h};
+  for (int i = 0; i < 12; ++i) {
+    if (strides[i] < 0) return EA_EUNSUPPORTED;
+    const int esz = i < 9 ? ein : eout;
+    if ((strides[i] * esz) % 16 != 0) return EA_EUNSUPPORTED;
+  }
+  if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->o)) return EA_EUNSUPPORTED;
+  if (a->lse != nullptr) {
+    if (((uintptr_t)a->lse & 3u) != 0 || a->lse_stride_b < 0 || a->lse_stride_h < 0) return EA_EUNSUPPORTED;
+  }
+  // the kernels keep per-head row offsets and tile indices in 32 bits
+  const int64_t lim = (int64_t)1 << 31;
+  if (N >= lim / 2 || B * H >= lim) return EA_EUNSUPPORTED;
+  for (int i = 0; i < 4; ++i) {
+    if (strides[3 * i + 1] * N >= lim) return EA_EUNSUPPORTED;
+  }
+
+  const Span so = span_of(a->o, B, N, H, D, a->o_stride_b, a->o_stride_s, a->o_stride_h, eout);
+  const Span sq = span_of(a->q, B, N, H, D, a->q_stride_b, a->q_stride_s, a->q_stride_h, ein);
+  const Span sk = span_of(a->k, B, N, H, D, a->k_stride_b, a->k_stride_s, a->k_stride_h, ein);
+  const Span sv = span_of(a->v, B, N, H, D, a->v_stride_b, a->v_stride_s, a->v_stride_h, ein);
+  if (overlaps(so, sq) || overlaps(so, sk) || overlaps(so, sv)) return EA_EINVAL;
+  return EA_OK;
+}
+
+ea::FwdParams make_params(const ea_attn_args* a) {
+  ea::FwdParams p;
+  p.q = a->q;
+  p.k = a->k;
+  p.v = a->v;
+  p.o = a->o;
+  p.lse = a->lse;
+  p.batch = (int)a->batch;
+  p.heads = (int)a->nheads_q;
+  p.n = (int)a->seqlen_q;
+  p.q_tiles = (p.n + ea::tile_bm() - 1) / ea::tile_bm();
+  p.q_sb = a->q_stride_b; p.q_ss = a->q_stride_s; p.q_sh = a->q_stride_h;
+  p.k_sb = a->k_stride_b; p.k_ss = a->k_stride_s; p.k_sh = a->k_stride_h;
+  p.v_sb = a->v_stride_b; p.v_ss = a->v_stride_s; p.v_sh = a->v_stride_h;
+  p.o_sb = a->o_stride_b; p.o_ss = a->o_stride_s; p.o_sh = a->o_stride_h;
+  p.lse_sb = a->lse_stride_b; p.lse_sh = a->lse_stride_h;
+  p.causal = a->causal ? 1 : 0;
+  p.wl = a->window_left;
+  p.wr = a->window_right;
+  const bool fp8 = a->in_dtype == EA_FP8_E4M3;
+  const double c = (double)a->softmax_scale * (fp8 ? (double)a->q_descale * (double)a->k_descale : 1.0) *
+                   1.4426950408889634;
+  p.c_log2 = (float)c;
+  p.v_descale = fp8 ? a->v_descale : 1.0f;
+  return p;
+}
+
+// Host-side mirror of the kernel's tile walk, for plan reports only.
+void count_tiles(const ea::FwdParams& p, int64_t* tiles, int64_t* masked) {
+  const int bm = ea::tile_bm(), bn = ea::tile_bn();
+  int64_t t_all = 0, t_mask = 0;
+  for (int t = 0; t < p.q_tiles; ++t) {
+    const int q0 = t * bm;
+    const int qlast = std::min(q0 + bm, p.n) - 1;
+    int lo = p.wl >= 0 ? std::max(0, q0 - p.wl) : 0;
+    int hi = p.n;
+    if (p.causal) hi = std::min(hi, qlast + 1);
+    if (p.wr >= 0) hi = std::min(hi, qlast + p.wr + 1);
+    hi = std::max(lo, hi);
+    for (int kt = lo / bn; kt < (hi + bn - 1) / bn; ++kt) {
+      const int k0 = kt * bn, k1 = k0 + bn;
+      bool full = k1 <= p.n;
+      if (p.causal && k1 - 1 > q0) full = false;
+      if (p.wl >= 0 && k0 < qlast - p.wl) full = false;
+      if (p.wr >= 0 && k1 - 1 > q0 + p.wr) full = false;
+      ++t_all;
+      if (!full) ++t_mask;
+    }
+  }
+  const int64_t bh = (int64_t)p.batch * p.heads;
+  *tiles = t_all * bh;
+  *masked = t_mask * bh;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ea_attn_fwd(const ea_attn_args* args, void* stream) {
+  bool empty = false;
+  const int st = validate(args, &empty);
+  if (st != EA_OK || empty) return st;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    g_last_hip_error = (int)e;
+    return EA_EHIP;
+  }
+  if (!device_is_gfx950(dev)) return EA_EDEVICE;
+  const ea::FwdParams p = make_params(args);
+  e = ea::launch_fwd(p, args->in_dtype, (int)args->headdim, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    g_last_hip_error = (int)e;
+    return EA_EHIP;
+  }
+  return EA_OK;
+}
+
+int ea_attn_plan(const ea_attn_args* args, ea_attn_plan_info* info) {
+  if (info == nullptr || info->struct_size < sizeof(ea_attn_plan_info)) return EA_EINVAL;
+  bool empty = false;
+  const int st = validate(args, &empty);
+  if (st != EA_OK) return st;
+  const uint32_t sz = info->struct_size;
+  std::memset(info, 0, sizeof(ea_attn_plan_info));
+  info->struct_size = sz;
+  info->block_m = ea::tile_bm();
+  info->block_n = ea::tile_bn();
+  info->waves = ea::tile_waves();
+  info->lds_bytes = ea::lds_bytes(args->in_dtype, (int)args->headdim);
+  std::strncpy(info->kernel, ea::kernel_name(args->in_dtype, (int)args->headdim), sizeof(info->kernel) - 1);
+  if (empty) return EA_OK;
+  const ea::FwdParams p = make_params(args);
+  info->grid = (int64_t)p.q_tiles * p.batch * p.heads;
+  count_tiles(p, &info->kv_tiles, &info->masked_tiles);
+  return EA_OK;
+}
+
+const char* ea_status_string(int status) {
+  switch (status) {
+    case EA_OK: return "ok";
+    case EA_EINVAL: return "invalid argument";
+    case EA_EUNSUPPORTED: return "unsupported argument combination";
+    case EA_EDEVICE: return "current device is not gfx950";
+    case EA_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int ea_last_hip_error(void) { return g_last_hip_error; }
+
+uint32_t ea_abi_version(void) { return EA_ABI_VERSION; }
+
+}  // extern "C"

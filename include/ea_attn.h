@@ -1,0 +1,158 @@
+/*
+ * ea_attn.h -- C ABI of the MI355X (gfx950) exact-attention forward library.
+ *
+ * The operation is exact scaled-dot-product attention,
+ *
+ *     O = softmax(Q K^T * scale + mask) V,      LSE_i = ln sum_j exp(s_ij)
+ *
+ * the "standard attention" of the "Flash Attention | Hermes Skill" page
+ * (Workflow 1, Step 2), computed with the IO-aware tiling its Quick start
+ * names: tiles live on chip and the softmax is online (running max / running
+ * sum), so the N x N score matrix never reaches HBM ("FlashAttention",
+ * aiunderstanding.org, sections "Djupdykning" and "Teknisk insikt").  The
+ * result equals the materialised definition up to floating-point rounding.
+ *
+ * Conventions shared by every call:
+ *   - Pointers named q, k, v, o, lse are DEVICE pointers on the current HIP
+ *     device.  The caller owns every buffer; the library allocates nothing,
+ *     keeps no buffer, and never modifies q, k or v.
+ *   - Strides are in ELEMENTS.  A tensor is addressed as
+ *       base + b*stride_b + s*stride_s + h*stride_h + d      (d contiguous)
+ *     which covers [batch, seqlen, nheads, headdim] ("bshd", the flash-attn
+ *     layout of the pages' Workflow 2), [batch, heads, seq, dim] ("bhsd", the
+ *     SDPA layout of the pages' Quick start) and transposed views of either,
+ *     without copies.
+ *   - Calls return an ea_status code and never abort, print or throw.
+ *   - The library is thread-safe: apart from a once-initialised table of
+ *     device properties it holds no mutable global state.
+ */
+#ifndef EA_ATTN_H
+#define EA_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define EA_ABI_VERSION 1u
+
+/* Status codes. */
+enum ea_status {
+  EA_OK = 0,
+  EA_EINVAL = 1,        /* malformed arguments: see ea_attn_fwd */
+  EA_EUNSUPPORTED = 2,  /* well-formed but outside what the kernels implement */
+  EA_EDEVICE = 3,       /* the current device is not a gfx950 GPU */
+  EA_EHIP = 4           /* a HIP runtime call failed; see ea_last_hip_error */
+};
+
+/* Element types. */
+enum ea_dtype {
+  EA_F16 = 1,           /* IEEE binary16 */
+  EA_BF16 = 2,          /* bfloat16 */
+  EA_FP8_E4M3 = 3,      /* OCP 8-bit float E4M3 ("fn": no infinities, max 448) */
+  EA_F32 = 4            /* accepted by the enum only to be rejected: the pages
+                           state that float32 inputs are not supported
+                           ("Flash Attention | Hermes Skill", Common issues) */
+};
+
+/*
+ * Arguments of one forward call.  struct_size must be sizeof(ea_attn_args)
+ * (the struct may grow at its end in later ABI versions).
+ */
+typedef struct ea_attn_args {
+  uint32_t struct_size;
+  int32_t in_dtype;          /* ea_dtype of q, k, v: EA_F16, EA_BF16 or EA_FP8_E4M3 */
+  int32_t out_dtype;         /* ea_dtype of o: same as in_dtype for 16-bit inputs,
+                                EA_BF16 for EA_FP8_E4M3 inputs */
+  int32_t causal;            /* nonzero: key j is visible from query i only if j <= i */
+  int32_t window_left;       /* sliding window, inclusive: keys j with */
+  int32_t window_right;      /*   i - window_left <= j <= i + window_right;
+                                -1 on a side means unbounded on that side
+                                (the pages' window_size=(left, right),
+                                "Flash Attention | Hermes Skill", Workflow 2) */
+  float softmax_scale;       /* finite and > 0; the pages' default is 1/sqrt(headdim) */
+  float q_descale;           /* fp8 only: the stored value times the descale is the */
+  float k_descale;           /*   real value (per-tensor scales); must be finite and */
+  float v_descale;           /*   > 0, and exactly 1.0 for 16-bit inputs */
+  int64_t batch;             /* B >= 0 */
+  int64_t seqlen_q;          /* Nq >= 0 */
+  int64_t seqlen_k;          /* Nk >= 0; this version requires Nq == Nk */
+  int64_t nheads_q;          /* Hq >= 1 */
+  int64_t nheads_k;          /* Hk >= 1; this version requires Hk == Hq */
+  int64_t headdim;           /* D: 64 or 128 */
+  const void* q;             /* [B, Nq, Hq, D] via the strides below */
+  const void* k;             /* [B, Nk, Hk, D] */
+  const void* v;             /* [B, Nk, Hk, D] */
+  void* o;                   /* [B, Nq, Hq, D], written in full */
+  float* lse;                /* [B, Hq, Nq] float32, natural log of the scaled,
+                                masked scores; NULL = do not write */
+  int64_t q_stride_b, q_stride_s, q_stride_h;
+  int64_t k_stride_b, k_stride_s, k_stride_h;
+  int64_t v_stride_b, v_stride_s, v_stride_h;
+  int64_t o_stride_b, o_stride_s, o_stride_h;
+  int64_t lse_stride_b, lse_stride_h;   /* LSE rows are contiguous along Nq */
+} ea_attn_args;
+
+/* What ea_attn_fwd would launch for a given argument set. */
+typedef struct ea_attn_plan_info {
+  uint32_t struct_size;      /* set by the caller to sizeof(ea_attn_plan_info) */
+  int32_t block_m;           /* query rows per workgroup */
+  int32_t block_n;           /* keys per K/V tile */
+  int32_t waves;             /* wavefronts per workgroup */
+  int32_t lds_bytes;         /* LDS per workgroup */
+  int64_t grid;              /* workgroups launched */
+  int64_t kv_tiles;          /* K/V tiles visited over the whole launch */
+  int64_t masked_tiles;      /* of which need per-element masking */
+  char kernel[64];           /* name of the kernel instantiation */
+} ea_attn_plan_info;
+
+/*
+ * ea_attn_fwd -- launch the attention forward on `stream` (a hipStream_t;
+ * NULL is the default stream).  Asynchronous: returns once the kernel is
+ * enqueued; no host synchronisation, no allocation.
+ *
+ * Checks its arguments and returns without launching anything on failure
+ * (o and lse are then untouched); the first failing check decides the code:
+ *   EA_EINVAL        args NULL or struct_size too small; a NULL q/k/v/o; a
+ *                    negative size; Hq or Hk < 1; a bad dtype enum; a
+ *                    non-finite softmax_scale; a descale that is not finite
+ *                    and > 0, or != 1 for 16-bit inputs; window bounds < -1;
+ *                    o overlapping q, k or v.
+ *   EA_EUNSUPPORTED  float32 inputs; headdim not 64 or 128 (fp8: not 128);
+ *                    Nq != Nk; Hq != Hk; softmax_scale <= 0; an output
+ *                    dtype other than the one above; a negative stride; a
+ *                    base pointer not 16-byte aligned or a b/s/h stride
+ *                    whose byte size is not a multiple of 16 (the kernels
+ *                    move 16-byte vectors); an lse pointer not 4-byte
+ *                    aligned; an index that would overflow 32 bits
+ *                    (|stride| * extent >= 2^31 elements).
+ *   EA_EDEVICE       the current device is not gfx950.
+ *   EA_EHIP          a HIP call or the launch failed.
+ * B == 0 or Nq == 0 returns EA_OK without launching once the dtype, size,
+ * scale, descale and window checks have passed (the pointers may be NULL).
+ */
+int ea_attn_fwd(const ea_attn_args* args, void* stream);
+
+/*
+ * ea_attn_plan -- fill *info with the tile configuration and grid that
+ * ea_attn_fwd would use for *args.  Runs the same argument checks except the
+ * device check, launches nothing and touches no device memory, so it works
+ * without a GPU.  info->struct_size must be set by the caller.
+ */
+int ea_attn_plan(const ea_attn_args* args, ea_attn_plan_info* info);
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char* ea_status_string(int status);
+
+/* The hipError_t of the last EA_EHIP failure on the calling thread (0 if none). */
+int ea_last_hip_error(void);
+
+/* EA_ABI_VERSION of the built library. */
+uint32_t ea_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EA_ATTN_H */

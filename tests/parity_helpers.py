@@ -1,0 +1,131 @@
+"""Shared pieces of the GPU parity tests: upload, run, compare with the oracle.
+
+Tolerances (derived in the design notes from the output formats):
+  * fp16 output: max |O_gpu - O_ref| <= 2e-3.
+  * bf16 output from bf16 inputs: |O_gpu - O_ref| <= 2e-3 + ulp_bf16(O_ref)
+    elementwise.  Rounding the exact result to bf16 alone can cost half an
+    ulp (7.8e-3 for |O| in [2, 4), which early causal rows reach), so a raw
+    2e-3 bound is out of reach of any bf16-output kernel.
+  * fp8 inputs (bf16 output): max |O_gpu - O_ref| <= 3e-2 against the oracle
+    on the dequantised inputs.
+  * LSE: max |LSE_gpu - LSE_ref| <= 1e-3 for every dtype.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+import oracle
+from exact_attention_04_amd import attention
+from exact_attention_04_amd.workloads import Inputs
+
+TOL_F16 = 2e-3
+TOL_BF16 = 2e-3
+TOL_FP8 = 3e-2
+TOL_LSE = 1e-3
+
+
+def stored_f64(t: torch.Tensor, descale: float) -> np.ndarray:
+    """Real values of stored inputs in float64 (fp8 decoded by the oracle)."""
+    if t.dtype == torch.float8_e4m3fn:
+        return oracle.dequantize_e4m3(t.view(torch.uint8).numpy(), descale)
+    return t.to(torch.float64).numpy()
+
+
+def ulp_bf16(x: np.ndarray) -> np.ndarray:
+    ax = np.abs(x)
+    e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
+    e = np.maximum(e, -126.0)
+    return np.ldexp(1.0, (e - 7).astype(np.int64))
+
+
+def upload(inp: Inputs, device="cuda"):
+    return tuple(t.to(device) for t in (inp.q, inp.k, inp.v))
+
+
+def run_gpu(inp: Inputs, *, causal=False, window=(-1, -1), scale=None, layout="bshd"):
+    q, k, v = upload(inp)
+    is_fp8 = inp.q.dtype == torch.float8_e4m3fn
+    o, lse = attention(q, k, v, causal=causal, window_size=window, softmax_scale=scale, layout=layout,
+                       descale=inp.descale if is_fp8 else None)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def compare(o_gpu: np.ndarray, o_ref: np.ndarray, lse_gpu: np.ndarray, lse_ref: np.ndarray, kind: str, what=""):
+    """Assert the R10/R11 criteria; returns a dict of the measured errors."""
+    assert o_gpu.shape == o_ref.shape, (o_gpu.shape, o_ref.shape)
+    assert np.isfinite(o_gpu).all(), f"{what}: non-finite output"
+    err = np.abs(o_gpu - o_ref)
+    res = {"max_abs": float(err.max()) if err.size else 0.0}
+    if kind == "f16":
+        assert res["max_abs"] <= TOL_F16, f"{what}: max |dO| {res['max_abs']:.3g} > {TOL_F16}"
+    elif kind == "bf16":
+        bound = TOL_BF16 + ulp_bf16(o_ref)
+        excess = err - bound
+        worst = float(excess.max()) if excess.size else -1.0
+        assert worst <= 0, f"{what}: |dO| exceeds 2e-3 + ulp_bf16 by {worst:.3g} (max |dO| {res['max_abs']:.3g})"
+    elif kind == "fp8":
+        assert res["max_abs"] <= TOL_FP8, f"{what}: max |dO| {res['max_abs']:.3g} > {TOL_FP8}"
+    else:
+        raise ValueError(kind)
+    if lse_gpu is not None:
+        fin = np.isfinite(lse_ref)
+        assert np.array_equal(np.isfinite(lse_gpu), fin), f"{what}: LSE finiteness differs"
+        lerr = float(np.abs(lse_gpu[fin] - lse_ref[fin]).max()) if fin.any() else 0.0
+        res["lse_max_abs"] = lerr
+        assert lerr <= TOL_LSE, f"{what}: max |dLSE| {lerr:.3g} > {TOL_LSE}"
+    return res
+
+
+def kind_of(dtype: str) -> str:
+    return {"f16": "f16", "bf16": "bf16", "fp8": "fp8"}[dtype]
+
+
+def full_check(inp: Inputs, dtype: str, *, causal=False, window=(-1, -1), scale=None, layout="bshd", what=""):
+    """Whole-tensor comparison against the oracle (small shapes)."""
+    o, lse = run_gpu(inp, causal=causal, window=window, scale=scale, layout=layout)
+    qf, kf, vf = (stored_f64(t, s) for t, s in zip((inp.q, inp.k, inp.v), inp.descale))
+    D = qf.shape[-1]
+    sc = 1.0 / math.sqrt(D) if scale is None else scale
+    o_ref, lse_ref = oracle.attention(qf, kf, vf, scale=sc, causal=causal, window=window, layout=layout)
+    return compare(o.float().cpu().double().numpy(), o_ref, lse.cpu().double().numpy(), lse_ref, kind_of(dtype), what)
+
+
+def sampled_check(inp: Inputs, dtype: str, o_gpu: torch.Tensor, lse_gpu: torch.Tensor, heads, rows, *,
+                  causal=False, window=(-1, -1), scale=None, layout="bshd", what=""):
+    """Compare listed (b, h) heads at listed query rows against the oracle."""
+    rows = np.asarray(sorted(set(int(r) for r in rows)))
+    sel_o, sel_l = [], []
+    for (b, h) in heads:
+        if layout == "bshd":
+            sel_o.append(o_gpu[b, rows, h, :].float().cpu().double().numpy())
+        else:
+            sel_o.append(o_gpu[b, h, rows, :].float().cpu().double().numpy())
+        sel_l.append(lse_gpu[b, h, rows].cpu().double().numpy())
+    # the oracle needs only the selected heads' inputs
+    def head_arr(t, s, b, h):
+        x = t[b, :, h, :] if layout == "bshd" else t[b, h, :, :]
+        return stored_f64(x.contiguous(), s)
+    o_refs, l_refs = [], []
+    for (b, h) in heads:
+        qf, kf, vf = (head_arr(t, s, b, h) for t, s in zip((inp.q, inp.k, inp.v), inp.descale))
+        sc = 1.0 / math.sqrt(qf.shape[-1]) if scale is None else scale
+        o1, l1 = oracle.attention_head(qf, kf, vf, sc, causal, window[0], window[1], rows=rows)
+        o_refs.append(o1)
+        l_refs.append(l1)
+    return compare(np.stack(sel_o), np.stack(o_refs), np.stack(sel_l), np.stack(l_refs), kind_of(dtype), what)
+
+
+def sample_rows(n: int, seed: int, extra: int = 96):
+    """Rows covering the start, tile edges, the end and random interior rows."""
+    rng = np.random.default_rng(seed)
+    rows = set(range(min(n, 64)))
+    for edge in (127, 128, 129, 255, 256, 4095, 4096, 4097, n // 2, n - 129, n - 128, n - 65, n - 64):
+        if 0 <= edge < n:
+            rows.add(edge)
+    rows.update(range(max(0, n - 32), n))
+    rows.update(int(r) for r in rng.integers(0, n, size=extra))
+    return sorted(rows)

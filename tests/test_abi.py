@@ -1,0 +1,173 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and its argument checks and planner behave as documented.
+
+No call here launches work: ea_attn_plan touches no device memory, and the
+ea_attn_fwd calls below all fail validation before any device is queried.
+"""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+from exact_attention_04_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ea_attn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libea_attn.so not built")
+
+FAKE = 0x7F0000000000   # never dereferenced: plan() and failing fwd() calls do not touch memory
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(ea_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_exactly_the_exports():
+    assert header_functions() == sorted(_lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    syms = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in header_functions():
+        assert name in syms, f"{name} not exported"
+        assert hasattr(_lib.lib(), name)
+
+
+def test_abi_version_and_status_strings():
+    assert _lib.lib().ea_abi_version() == _lib.EA_ABI_VERSION
+    for code in range(5):
+        assert _lib.status_string(code)
+    assert _lib.status_string(99) == "unknown status"
+    assert _lib.lib().ea_last_hip_error() == 0
+
+
+def test_struct_sizes_match_c():
+    # same layout rules as the C compiler on x86-64 / amdgcn
+    assert ctypes.sizeof(_lib.AttnArgs) == 4 + 5 * 4 + 4 * 4 + 6 * 8 + 5 * 8 + 14 * 8
+    assert ctypes.sizeof(_lib.PlanInfo) == 4 + 4 * 4 + 4 + 3 * 8 + 64
+
+
+def make(B=2, N=300, H=3, D=128, dtype=_lib.EA_BF16, layout="bshd", **kw):
+    a = _lib.AttnArgs()
+    a.struct_size = ctypes.sizeof(_lib.AttnArgs)
+    a.in_dtype = dtype
+    a.out_dtype = _lib.EA_BF16 if dtype == _lib.EA_FP8_E4M3 else dtype
+    a.softmax_scale = 1.0 / math.sqrt(D)
+    a.q_descale = a.k_descale = a.v_descale = 1.0
+    a.window_left = a.window_right = -1
+    a.batch, a.seqlen_q, a.seqlen_k, a.nheads_q, a.nheads_k, a.headdim = B, N, N, H, H, D
+    size = B * N * H * D * 4 + 4096
+    a.q, a.k, a.v, a.o = FAKE, FAKE + size, FAKE + 2 * size, FAKE + 3 * size
+    if layout == "bshd":
+        sb, ss, sh = N * H * D, H * D, D
+    else:
+        sb, ss, sh = N * H * D, D, N * D
+    for t in "qkvo":
+        setattr(a, f"{t}_stride_b", sb)
+        setattr(a, f"{t}_stride_s", ss)
+        setattr(a, f"{t}_stride_h", sh)
+    a.lse = FAKE + 4 * size
+    a.lse_stride_b, a.lse_stride_h = H * N, N
+    for k_, v_ in kw.items():
+        setattr(a, k_, v_)
+    return a
+
+
+def plan_status(a):
+    info = _lib.PlanInfo()
+    info.struct_size = ctypes.sizeof(_lib.PlanInfo)
+    return _lib.lib().ea_attn_plan(ctypes.byref(a), ctypes.byref(info)), info
+
+
+def test_plan_valid_configs():
+    for dtype, D in ((_lib.EA_F16, 64), (_lib.EA_BF16, 128), (_lib.EA_FP8_E4M3, 128)):
+        for layout in ("bshd", "bhsd"):
+            st, info = plan_status(make(dtype=dtype, D=D, layout=layout))
+            assert st == _lib.EA_OK, _lib.status_string(st)
+            assert info.block_m == 128 and info.block_n == 64 and info.waves == 4
+            assert info.grid == 2 * 3 * math.ceil(300 / 128)
+            assert info.kernel.decode().startswith("attn_fwd<")
+            assert info.lds_bytes <= 160 * 1024
+
+
+def test_plan_tile_counts_causal_and_window():
+    # causal N=4096: query tile t (128 rows) visits 2t+2 key tiles of 64
+    st, info = plan_status(make(B=1, N=4096, H=1, causal=1))
+    assert st == 0
+    assert info.kv_tiles == sum(2 * t + 2 for t in range(32))
+    assert info.masked_tiles == 32 * 2
+    st, info = plan_status(make(B=1, N=4096, H=1))
+    assert info.kv_tiles == 32 * 64 and info.masked_tiles == 0
+    # window [i-4095, i] at N=16384: at most 66 key tiles per query tile
+    st, info = plan_status(make(B=1, N=16384, H=1, causal=1, window_left=4095, window_right=0))
+    assert st == 0
+    assert info.kv_tiles <= 128 * 66
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("struct_size", 8, _lib.EA_EINVAL),
+    ("batch", -1, _lib.EA_EINVAL),
+    ("nheads_q", 0, _lib.EA_EINVAL),
+    ("in_dtype", 9, _lib.EA_EINVAL),
+    ("softmax_scale", float("nan"), _lib.EA_EINVAL),
+    ("softmax_scale", float("inf"), _lib.EA_EINVAL),
+    ("q_descale", 2.0, _lib.EA_EINVAL),            # descale != 1 on 16-bit input
+    ("window_left", -2, _lib.EA_EINVAL),
+    ("q", 0, _lib.EA_EINVAL),
+    ("o", FAKE, _lib.EA_EINVAL),                    # o aliases q
+    ("in_dtype", _lib.EA_F32, _lib.EA_EUNSUPPORTED),  # fp32 input
+    ("headdim", 96, _lib.EA_EUNSUPPORTED),
+    ("seqlen_k", 299, _lib.EA_EUNSUPPORTED),
+    ("nheads_k", 1, _lib.EA_EUNSUPPORTED),
+    ("out_dtype", _lib.EA_F16, _lib.EA_EUNSUPPORTED),
+    ("softmax_scale", -0.5, _lib.EA_EUNSUPPORTED),
+    ("q", FAKE + 8, _lib.EA_EUNSUPPORTED),          # not 16-byte aligned
+    ("k_stride_s", 128 * 3 + 4, _lib.EA_EUNSUPPORTED),  # row stride not a 16-byte multiple
+    ("v_stride_h", -128, _lib.EA_EUNSUPPORTED),
+    ("lse", FAKE + 2, _lib.EA_EUNSUPPORTED),
+])
+def test_validation_errors(field, value, code):
+    a = make()
+    setattr(a, field, value)
+    st, _ = plan_status(a)
+    assert st == code, (field, value, _lib.status_string(st))
+    # the launch entry point applies the same checks before touching a device
+    assert _lib.lib().ea_attn_fwd(ctypes.byref(a), None) == code
+
+
+def test_fp8_argument_rules():
+    a = make(dtype=_lib.EA_FP8_E4M3, q_descale=0.01, k_descale=0.02, v_descale=0.03)
+    assert plan_status(a)[0] == _lib.EA_OK
+    assert plan_status(make(dtype=_lib.EA_FP8_E4M3, q_descale=0.0))[0] == _lib.EA_EINVAL
+    assert plan_status(make(dtype=_lib.EA_FP8_E4M3, out_dtype=_lib.EA_F16))[0] == _lib.EA_EUNSUPPORTED
+    assert plan_status(make(dtype=_lib.EA_FP8_E4M3, D=64))[0] == _lib.EA_EUNSUPPORTED
+
+
+def test_empty_problem_is_ok_without_pointers():
+    a = make(B=0)
+    a.q = a.k = a.v = a.o = 0
+    st, info = plan_status(a)
+    assert st == _lib.EA_OK and info.grid == 0
+    assert _lib.lib().ea_attn_fwd(ctypes.byref(a), None) == _lib.EA_OK
+    a = make(N=0)
+    assert _lib.lib().ea_attn_fwd(ctypes.byref(a), None) == _lib.EA_OK
+
+
+def test_plan_rejects_small_info_struct():
+    info = _lib.PlanInfo()
+    info.struct_size = 4
+    assert _lib.lib().ea_attn_plan(ctypes.byref(make()), ctypes.byref(info)) == _lib.EA_EINVAL
+
+
+def test_python_wrapper_rejects_cpu_tensors():
+    import torch
+    from exact_attention_04_amd import attention
+    x = torch.zeros(1, 8, 1, 64, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        attention(x, x, x)

@@ -1,0 +1,90 @@
+"""GPU parity: the HIP path against the float64 oracle on the same seeded inputs.
+
+Small shapes are compared element by element over whole tensors (several
+query tiles and key tiles, ragged tails, every mask kind).  The named
+workloads run at full size in the launch configuration the benchmark times,
+and are compared on sampled heads and rows that the oracle computes one by
+one.
+"""
+import numpy as np
+import pytest
+import torch
+
+from exact_attention_04_amd.workloads import WORKLOADS, make_inputs, small_case
+from parity_helpers import full_check, run_gpu, sample_rows, sampled_check
+
+pytestmark = pytest.mark.gpu
+
+MASKS = {
+    "none": (False, (-1, -1)),
+    "causal": (True, (-1, -1)),
+    "causal_w3": (True, (3, 0)),
+    "w17_5": (False, (17, 5)),
+    "diag": (False, (0, 0)),
+    "right0": (False, (-1, 0)),
+    "causal_w100": (True, (100, -1)),
+}
+
+
+@pytest.mark.parametrize("mask", list(MASKS))
+@pytest.mark.parametrize("n", [1, 7, 63, 64, 65, 127, 129, 200, 1000])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_small_sweep(dtype, d, n, mask):
+    causal, window = MASKS[mask]
+    seed = 1000 * d + n + 7 * list(MASKS).index(mask) + (0 if dtype == "f16" else 500000)
+    inp = small_case(2, 3, n, d, dtype, "bshd", seed)
+    full_check(inp, dtype, causal=causal, window=window, what=f"{dtype} d{d} n{n} {mask}")
+
+
+@pytest.mark.parametrize("layout", ["bshd", "bhsd"])
+@pytest.mark.parametrize("mask", ["none", "causal", "w17_5"])
+def test_layouts(layout, mask):
+    causal, window = MASKS[mask]
+    inp = small_case(2, 4, 333, 64, "f16", layout, 77)
+    full_check(inp, "f16", causal=causal, window=window, layout=layout, what=f"{layout} {mask}")
+
+
+@pytest.mark.parametrize("mask", ["none", "causal", "causal_w100", "w17_5"])
+@pytest.mark.parametrize("n", [1, 65, 300, 1000])
+def test_fp8_small(n, mask):
+    causal, window = MASKS[mask]
+    inp = small_case(1, 3, n, 128, "fp8", "bshd", 9000 + n)
+    full_check(inp, "fp8", causal=causal, window=window, what=f"fp8 n{n} {mask}")
+
+
+def test_explicit_scale():
+    inp = small_case(1, 2, 257, 64, "f16", "bhsd", 5)
+    full_check(inp, "f16", causal=True, scale=1.0 / 8.0, layout="bhsd", what="scale 1/8")
+    full_check(inp, "f16", causal=False, scale=0.37, layout="bhsd", what="scale 0.37")
+
+
+# ---------------------------------------------------------------------------
+# The named workloads at full size
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["sdpa_b1h8n512d64_f16", "sdpa_b2h8n2048d64_f16", "sdpa_b2h8n2048d64_f16_causal"])
+def test_workload_full(name):
+    w = WORKLOADS[name]
+    inp = make_inputs(w)
+    r = full_check(inp, w.dtype, causal=w.causal, window=(w.window_left, w.window_right), scale=w.softmax_scale,
+                   layout=w.layout, what=name)
+    print(name, r)
+
+
+@pytest.mark.parametrize("name", ["sdpa_b4h32n4096d128_bf16_causal", "swa_b1h32n16384d128_bf16_w4095",
+                                  "fp8_b1h16n65536d128_causal"])
+def test_workload_sampled(name):
+    w = WORKLOADS[name]
+    inp = make_inputs(w)
+    window = (w.window_left, w.window_right)
+    o, lse = run_gpu(inp, causal=w.causal, window=window, scale=w.softmax_scale, layout=w.layout)
+    assert torch.isfinite(o.float()).all().item()
+    assert torch.isfinite(lse).all().item()
+    rng = np.random.default_rng(w.seed)
+    heads = [(0, 0), (w.batch - 1, w.heads - 1)]
+    heads += [(int(rng.integers(w.batch)), int(rng.integers(w.heads))) for _ in range(2)]
+    rows = sample_rows(w.seqlen, w.seed)
+    r = sampled_check(inp, w.dtype, o, lse, heads, rows, causal=w.causal, window=window, scale=w.softmax_scale,
+                      layout=w.layout, what=name)
+    print(name, r)

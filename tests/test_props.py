@@ -1,0 +1,119 @@
+"""GPU properties of the HIP path that hold exactly (bitwise) or by construction.
+
+  * repeated calls give identical bits (no atomics, no races in LDS);
+  * the BSHD and BHSD layouts and transposed views give identical bits;
+  * equivalent masks give identical bits: causal == window(-1, 0) ==
+    window(N, 0) with causal, and a window wider than N == no window;
+  * constant V gives constant O (within the output tolerance);
+  * the call allocates no device memory of its own (the memory stays linear
+    in N: "FlashAttention", aiunderstanding.org, "Teknisk insikt").
+"""
+import numpy as np
+import pytest
+import torch
+
+from exact_attention_04_amd import attention
+from exact_attention_04_amd.workloads import small_case
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu(inp):
+    return tuple(t.cuda() for t in (inp.q, inp.k, inp.v))
+
+
+def _same(a, b):
+    return torch.equal(a.view(torch.uint8) if a.dtype != torch.float32 else a, b.view(torch.uint8) if b.dtype != torch.float32 else b)
+
+
+@pytest.mark.parametrize("dtype,d", [("f16", 64), ("bf16", 128)])
+def test_deterministic(dtype, d):
+    q, k, v = _gpu(small_case(2, 4, 777, d, dtype, "bshd", 1))
+    o1, l1 = attention(q, k, v, causal=True)
+    o2, l2 = attention(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_layouts_bitwise_equal():
+    q, k, v = _gpu(small_case(2, 3, 300, 128, "bf16", "bshd", 2))
+    o1, l1 = attention(q, k, v, causal=True, layout="bshd")
+    qt, kt, vt = (x.transpose(1, 2).contiguous() for x in (q, k, v))
+    o2, l2 = attention(qt, kt, vt, causal=True, layout="bhsd")
+    # a non-contiguous BHSD view of BSHD storage
+    o3, l3 = attention(q.transpose(1, 2), k.transpose(1, 2), v.transpose(1, 2), causal=True, layout="bhsd")
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2.transpose(1, 2)) and torch.equal(l1, l2)
+    assert torch.equal(o1, o3.transpose(1, 2)) and torch.equal(l1, l3)
+
+
+@pytest.mark.parametrize("n", [64, 333])
+def test_equivalent_masks_bitwise(n):
+    q, k, v = _gpu(small_case(1, 2, n, 64, "f16", "bshd", 3))
+    ref = attention(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    for causal, win in [(False, (-1, 0)), (True, (n, 0)), (True, (-1, 7)), (True, (n + 100, -1))]:
+        o, l = attention(q, k, v, causal=causal, window_size=win)
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref[0]) and torch.equal(l, ref[1]), (causal, win)
+    full = attention(q, k, v)
+    wide = attention(q, k, v, window_size=(n, n))
+    torch.cuda.synchronize()
+    assert torch.equal(full[0], wide[0]) and torch.equal(full[1], wide[1])
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_constant_v(dtype):
+    inp = small_case(1, 2, 500, 128, dtype, "bshd", 4)
+    q, k, v = _gpu(inp)
+    c = torch.linspace(-3, 3, 128, device="cuda").to(v.dtype)
+    v = c.view(1, 1, 1, 128).expand_as(v).contiguous()
+    for causal, win in [(False, (-1, -1)), (True, (-1, -1)), (True, (31, 0))]:
+        o, _ = attention(q, k, v, causal=causal, window_size=win)
+        torch.cuda.synchronize()
+        cref = c.double().view(1, 1, 1, 128).expand_as(o)
+        err = (o.double() - cref).abs()
+        bound = 2e-3 + (cref.abs() * 2.0 ** -7 if dtype == "bf16" else 0.0)
+        assert bool((err <= bound).all()), float(err.max())
+
+
+def test_no_device_allocation():
+    q, k, v = _gpu(small_case(2, 4, 1024, 128, "bf16", "bshd", 5))
+    o = torch.empty_like(q)
+    lse = torch.empty(2, 4, 1024, dtype=torch.float32, device="cuda")
+    attention(q, k, v, causal=True, out=o, lse=lse)
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    before = torch.cuda.memory_allocated()
+    attention(q, k, v, causal=True, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.cuda.max_memory_allocated() == before
+
+
+def test_lse_optional_and_strided():
+    q, k, v = _gpu(small_case(2, 3, 200, 64, "bf16", "bshd", 6))
+    o1, l1 = attention(q, k, v, causal=True)
+    o2, l2 = attention(q, k, v, causal=True, return_lse=False)
+    big = torch.full((2, 5, 256), 7.0, device="cuda")
+    lse_view = big[:, 1:4, 10:210]
+    o3, _ = attention(q, k, v, causal=True, lse=lse_view)
+    torch.cuda.synchronize()
+    assert l2 is None
+    assert torch.equal(o1, o2) and torch.equal(o1, o3)
+    assert torch.equal(lse_view, l1)
+    assert bool((big[:, 0] == 7).all()) and bool((big[:, 4] == 7).all()) and bool((big[:, 1:4, :10] == 7).all())
+
+
+def test_empty_inputs():
+    q = torch.empty(0, 16, 2, 64, dtype=torch.float16, device="cuda")
+    o, l = attention(q, q, q)
+    assert o.shape == q.shape and l.shape == (0, 2, 16)
+    q = torch.empty(2, 0, 2, 64, dtype=torch.float16, device="cuda")
+    o, l = attention(q, q, q, causal=True)
+    assert o.shape == q.shape
+
+
+def test_rejects_fp32_inputs():
+    q = torch.zeros(1, 8, 1, 64, dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError):
+        attention(q, q, q)
