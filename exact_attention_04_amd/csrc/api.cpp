@@ -4,6 +4,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 
@@ -117,7 +118,32 @@ int validate(const ea_attn_args* a, bool* empty) {
   return EA_OK;
 }
 
-ea::FwdParams make_params(const ea_attn_args* a) {
+// Tile configuration (see fwd_kernel.h).  The environment variable
+// EA_ATTN_TILE=bm128|bm256 overrides the choice (for tile sweeps); otherwise
+// the 128-row configuration is used.
+int choose_cfg(const ea_attn_args* /*a*/) {
+  static const int forced = [] {
+    const char* e = std::getenv("EA_ATTN_TILE");
+    if (e == nullptr) return -1;
+    if (std::strcmp(e, "bm128") == 0) return 0;
+    if (std::strcmp(e, "bm256") == 0) return 1;
+    return -1;
+  }();
+  if (forced >= 0) return forced;
+  return 0;
+}
+
+// Workgroup order (see the kernel).  EA_ATTN_SCHED=0|1 overrides it.
+int choose_sched() {
+  static const int forced = [] {
+    const char* e = std::getenv("EA_ATTN_SCHED");
+    if (e == nullptr) return -1;
+    return std::atoi(e) == 0 ? 0 : 1;
+  }();
+  return forced >= 0 ? forced : 0;
+}
+
+ea::FwdParams make_params(const ea_attn_args* a, int cfg) {
   ea::FwdParams p;
   p.q = a->q;
   p.k = a->k;
@@ -127,7 +153,7 @@ ea::FwdParams make_params(const ea_attn_args* a) {
   p.batch = (int)a->batch;
   p.heads = (int)a->nheads_q;
   p.n = (int)a->seqlen_q;
-  p.q_tiles = (p.n + ea::tile_bm() - 1) / ea::tile_bm();
+  p.q_tiles = (p.n + ea::tile_bm(cfg) - 1) / ea::tile_bm(cfg);
   p.q_sb = a->q_stride_b; p.q_ss = a->q_stride_s; p.q_sh = a->q_stride_h;
   p.k_sb = a->k_stride_b; p.k_ss = a->k_stride_s; p.k_sh = a->k_stride_h;
   p.v_sb = a->v_stride_b; p.v_ss = a->v_stride_s; p.v_sh = a->v_stride_h;
@@ -141,12 +167,13 @@ ea::FwdParams make_params(const ea_attn_args* a) {
                    1.4426950408889634;
   p.c_log2 = (float)c;
   p.v_descale = fp8 ? a->v_descale : 1.0f;
+  p.sched = choose_sched();
   return p;
 }
 
 // Host-side mirror of the kernel's tile walk, for plan reports only.
-void count_tiles(const ea::FwdParams& p, int64_t* tiles, int64_t* masked) {
-  const int bm = ea::tile_bm(), bn = ea::tile_bn();
+void count_tiles(const ea::FwdParams& p, int cfg, int64_t* tiles, int64_t* masked) {
+  const int bm = ea::tile_bm(cfg), bn = ea::tile_bn();
   int64_t t_all = 0, t_mask = 0;
   for (int t = 0; t < p.q_tiles; ++t) {
     const int q0 = t * bm;
@@ -186,8 +213,9 @@ int ea_attn_fwd(const ea_attn_args* args, void* stream) {
     return EA_EHIP;
   }
   if (!device_is_gfx950(dev)) return EA_EDEVICE;
-  const ea::FwdParams p = make_params(args);
-  e = ea::launch_fwd(p, args->in_dtype, (int)args->headdim, (hipStream_t)stream);
+  const int cfg = choose_cfg(args);
+  const ea::FwdParams p = make_params(args, cfg);
+  e = ea::launch_fwd(p, args->in_dtype, (int)args->headdim, cfg, (hipStream_t)stream);
   if (e != hipSuccess) {
     g_last_hip_error = (int)e;
     return EA_EHIP;
@@ -203,15 +231,16 @@ int ea_attn_plan(const ea_attn_args* args, ea_attn_plan_info* info) {
   const uint32_t sz = info->struct_size;
   std::memset(info, 0, sizeof(ea_attn_plan_info));
   info->struct_size = sz;
-  info->block_m = ea::tile_bm();
+  const int cfg = choose_cfg(args);
+  info->block_m = ea::tile_bm(cfg);
   info->block_n = ea::tile_bn();
-  info->waves = ea::tile_waves();
+  info->waves = ea::tile_waves(cfg);
   info->lds_bytes = ea::lds_bytes(args->in_dtype, (int)args->headdim);
-  std::strncpy(info->kernel, ea::kernel_name(args->in_dtype, (int)args->headdim), sizeof(info->kernel) - 1);
+  std::strncpy(info->kernel, ea::kernel_name(args->in_dtype, (int)args->headdim, cfg), sizeof(info->kernel) - 1);
   if (empty) return EA_OK;
-  const ea::FwdParams p = make_params(args);
+  const ea::FwdParams p = make_params(args, cfg);
   info->grid = (int64_t)p.q_tiles * p.batch * p.heads;
-  count_tiles(p, &info->kv_tiles, &info->masked_tiles);
+  count_tiles(p, cfg, &info->kv_tiles, &info->masked_tiles);
   return EA_OK;
 }
 

@@ -19,15 +19,18 @@ struct FwdParams {
   int64_t o_sb, o_ss, o_sh;
   int64_t lse_sb, lse_sh;
   int causal, wl, wr;
+  int sched;             // workgroup order: 0 = heaviest tiles first, 1 = per-XCD head-major
   float c_log2;          // softmax_scale * q_descale * k_descale * log2(e)
   float v_descale;
 };
 
-int tile_bm();
+// Tile configurations: 0 = 128 query rows per workgroup (32 per wave, two
+// waves per SIMD), 1 = 256 query rows (64 per wave, one wave per SIMD).
+int tile_bm(int cfg);
+int tile_waves(int cfg);
 int tile_bn();
-int tile_waves();
 int lds_bytes(int in_dtype, int d);
-const char* kernel_name(int in_dtype, int d);
-hipError_t launch_fwd(const FwdParams& p, int in_dtype, int d, hipStream_t stream);
+const char* kernel_name(int in_dtype, int d, int cfg);
+hipError_t launch_fwd(const FwdParams& p, int in_dtype, int d, int cfg, hipStream_t stream);
 
 }  // namespace ea

@@ -7,26 +7,36 @@
 // never written to HBM and the whole attention is one kernel.
 //
 // How it maps onto a CDNA4 compute unit:
-//   * 4 wavefronts x 32 query rows = 128 rows per workgroup (BM); K/V tiles of
-//     64 keys (BN) are staged in LDS, double buffered, shared by the 4 waves.
-//   * Each wave computes S^T = K Q^T on v_mfma_f32_32x32x16_{bf16,f16}
-//     (v_mfma_scale_f32_32x32x64_f8f6f4 for fp8): K (the A operand) comes
-//     from LDS, Q^T (the B operand) stays in registers for the whole kernel.
-//     In the 32x32 accumulator layout lane l holds column l%32, i.e. one
-//     query row, and 16 of the 32 keys; lane l^32 holds the other 16.  A row
-//     max therefore needs one exchange between the two wave halves, and the
-//     row sum needs none until the epilogue.
-//   * P^T leaves the accumulator already in the B-operand layout of
-//     O^T += V^T P^T (after a bf16/f16 conversion), so P never touches LDS.
-//     V^T fragments come from LDS with ds_read_b64_tr_b16 (transposing read).
-//   * LDS rows are XOR-swizzled in 16-byte units so that both the K reads
-//     (32 rows, same column) and the transposing V reads (4 rows x 64 bytes)
-//     hit 64 distinct banks per half-wave.
-//   * The running max is only moved (and O, l rescaled) when it grows by
-//     more than 2^8 in the exp2 domain; O and l always share the same
-//     reference, so O/l is unchanged in exact arithmetic.
-//   * Only tiles that cross the causal diagonal, the window edge or the end
-//     of the sequence evaluate the mask; tiles outside the visible range are
+//   * A workgroup is 4 waves; each wave owns RB blocks of 32 query rows
+//     (RB = 1: 128 rows per workgroup, two waves per SIMD; RB = 2: 256 rows,
+//     one wave per SIMD).  K/V tiles of 64 keys are staged in LDS, double
+//     buffered, by direct global-to-LDS loads.
+//   * S^T = K Q^T on v_mfma_f32_32x32x16_{bf16,f16} (fp8:
+//     v_mfma_scale_f32_32x32x64_f8f6f4).  K (A operand) comes from LDS and
+//     each K fragment feeds every row block; Q^T (B operand) stays in
+//     registers.  In the 32x32 accumulator lane l holds column l%32 -- one
+//     query row -- and 16 of 32 keys; lane l^32 holds the other 16, so a row
+//     max needs one exchange between wave halves and the row sum none until
+//     the epilogue.
+//   * P^T leaves the accumulator in the B-operand layout of O^T += V^T P^T
+//     (after a 16-bit conversion), so P never touches LDS; V^T fragments come
+//     from LDS with ds_read_b64_tr_b16 and feed every row block.
+//   * Issue is in order per wave, so matrix and vector work overlap only if
+//     they are interleaved in program order: a 64-key tile is processed as
+//     two 32-key halves a, b with
+//        S_a | max_a | S_b MFMAs interleaved with exp(S_a) |
+//        max_b | P_a.V MFMAs interleaved with exp(S_b) | P_b.V
+//   * LDS rows are XOR-swizzled in 16-byte units so the K reads (32 rows, one
+//     column) and the transposing V reads (4 rows x 64 bytes) are free of
+//     bank conflicts.
+//   * Softmax reference: each row's reference max is fixed at the first block
+//     where it sees a key, so O and l are never rescaled inside the loop.
+//     p = exp2((s - m_ref) c) may exceed 1 by a bounded factor; a row whose
+//     scores climb past that bound makes the workgroup repeat its key loop
+//     with the exact row maximum (rare: scores would have to grow by more
+//     than 2^15 / 2^64 in the exp2 domain after the first block).
+//   * Only tiles that cross the causal diagonal, a window edge or the end of
+//     the sequence evaluate the mask; tiles outside the visible range are
 //     never loaded.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -38,23 +48,20 @@ namespace ea {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
-constexpr int kBM = 32 * kWaves;   // query rows per workgroup
 constexpr int kBN = 64;            // keys per K/V tile
 constexpr float kLn2 = 0.6931471805599453f;
-// Largest growth of the running max (in log2 units) tolerated before O and l
-// are rescaled: p <= 2^8 stays far from fp16/bf16/fp32 overflow.
-constexpr float kRescaleThreshold = 8.0f;
 
 enum class In { F16, BF16, FP8 };
 
 // ---------------------------------------------------------------------------
-// LDS layout: a K or V tile is kBN rows of `row_bytes` bytes, split into
+// LDS layout: a K or V tile is kBN rows of ROW_BYTES bytes, split into
 // 16-byte units.  Unit u of row r is stored at unit u ^ swz(r).
 //   256-byte rows (16 units, d=128 at 16 bits): swz = ((r&3)<<2) | ((r>>2)&3)
 //   128-byte rows (8 units, d=64 at 16 bits or d=128 at 8 bits):
@@ -90,25 +97,32 @@ __device__ __forceinline__ f32x16 mfma_16bit(uint4 a, uint4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
-// Pack two fp32 values into the P operand type (round to nearest even).
-template <In IN>
-__device__ __forceinline__ uint32_t pack2(float a, float b) {
-  if constexpr (IN == In::F16) {
-    _Float16 x = (_Float16)a, y = (_Float16)b;
-    return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
-  } else {
-    __bf16 x = (__bf16)a, y = (__bf16)b;
-    return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
-  }
+__device__ __forceinline__ f32x16 mfma_fp8(uint4 a0, uint4 a1, uint4 b0, uint4 b1, f32x16 c) {
+  const i32x8 av = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+  const i32x8 bv = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+  // formats 0/0: both operands OCP e4m3; scale exponents 127: no block scaling
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 0, 0, 0, 127, 0, 127);
 }
 
-// Store 4 consecutive output elements (fp32 -> output type, RNE).
+// Pack two fp32 values into the P operand type (round to nearest even):
+// one v_cvt_pk_{bf16,f16}_f32.
 template <In IN>
-__device__ __forceinline__ void store4(void* dst, float a, float b, float c, float d) {
-  uint2 w;
-  if constexpr (IN == In::F16) { w.x = pack2<In::F16>(a, b); w.y = pack2<In::F16>(c, d); }
-  else { w.x = pack2<In::BF16>(a, b); w.y = pack2<In::BF16>(c, d); }
-  *(uint2*)dst = w;
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  const f32x2 v = {a, b};
+  if constexpr (IN == In::F16) return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+  else return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// Value of the low / high 16-bit half of a packed pair, as fp32.
+template <In IN>
+__device__ __forceinline__ float unpack_lo(uint32_t w) {
+  if constexpr (IN == In::F16) return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+  else return __builtin_bit_cast(float, w << 16);
+}
+template <In IN>
+__device__ __forceinline__ float unpack_hi(uint32_t w) {
+  if constexpr (IN == In::F16) return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+  else return __builtin_bit_cast(float, w & 0xffff0000u);
 }
 
 // fp8 e4m3 x16 (one uint4) -> bf16 x16 (two uint4), exact.
@@ -117,10 +131,10 @@ __device__ __forceinline__ void fp8x16_to_bf16(uint4 in, uint4& lo, uint4& hi) {
   uint32_t o[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    float a = __builtin_amdgcn_cvt_f32_fp8((int)w[i], 0);
-    float b = __builtin_amdgcn_cvt_f32_fp8((int)w[i], 1);
-    float c = __builtin_amdgcn_cvt_f32_fp8((int)w[i], 2);
-    float d = __builtin_amdgcn_cvt_f32_fp8((int)w[i], 3);
+    const float a = __builtin_amdgcn_cvt_f32_fp8((int)w[i], 0);
+    const float b = __builtin_amdgcn_cvt_f32_fp8((int)w[i], 1);
+    const float c = __builtin_amdgcn_cvt_f32_fp8((int)w[i], 2);
+    const float d = __builtin_amdgcn_cvt_f32_fp8((int)w[i], 3);
     o[2 * i] = pack2<In::BF16>(a, b);
     o[2 * i + 1] = pack2<In::BF16>(c, d);
   }
@@ -128,16 +142,20 @@ __device__ __forceinline__ void fp8x16_to_bf16(uint4 in, uint4& lo, uint4& hi) {
   hi = make_uint4(o[4], o[5], o[6], o[7]);
 }
 
-// Visible-key range of a query tile [q0, q0+BM) and the mask classification of
-// a key tile.  Mirrors the mask definition: key j visible from query i iff
-// j < n, (!causal || j <= i), (wl < 0 || j >= i - wl), (wr < 0 || j <= i + wr).
+// Max over the two lanes l, l^32 of a wave (they hold the two key halves of
+// one query row).
+__device__ __forceinline__ float pair_max(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
+
+// Visible-key range of query rows [q0, q0+qrows) and the mask classification
+// of a block of rows x keys.  Key j is visible from query i iff j < n,
+// (!causal || j <= i), (wl < 0 || j >= i - wl) and (wr < 0 || j <= i + wr).
 struct KeyRange {
-  int lo, hi;   // [lo, hi) keys that any row of the tile can see
+  int lo, hi;   // [lo, hi) keys that any of the rows can see
 };
 
 __device__ __forceinline__ KeyRange tile_key_range(int q0, int qrows, int n, int causal, int wl, int wr) {
-  int qlast = min(q0 + qrows, n) - 1;
-  int lo = wl >= 0 ? max(0, q0 - wl) : 0;
+  const int qlast = min(q0 + qrows, n) - 1;
+  const int lo = wl >= 0 ? max(0, q0 - wl) : 0;
   int hi = n;
   if (causal) hi = min(hi, qlast + 1);
   if (wr >= 0) hi = min(hi, qlast + wr + 1);
@@ -162,97 +180,110 @@ __device__ __forceinline__ bool block_none_visible(int r0, int r1, int k0, int k
   return false;
 }
 
-// Value of the low / high 16-bit half of a packed pair, as fp32.
-template <In IN>
-__device__ __forceinline__ float unpack_lo(uint32_t w) {
-  if constexpr (IN == In::F16) return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
-  else return __builtin_bit_cast(float, w << 16);
-}
-template <In IN>
-__device__ __forceinline__ float unpack_hi(uint32_t w) {
-  if constexpr (IN == In::F16) return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
-  else return __builtin_bit_cast(float, w & 0xffff0000u);
-}
-
-// O^T += V^T P^T over one 64-key tile.  P^T (16-bit, B operand) is in the
-// layout the S^T accumulator left it: lane l holds query l%32 and, for
-// k-step (kb, j0), keys 32 kb + 8 j0 + {4 half + t, 8 + 4 half + t}, t < 4.
-// The matching V^T fragment (A operand: row d = l%32 of the 32-column block,
-// the same 8 keys) is gathered with two transposing LDS reads: within each
-// 16-lane group, source lane sl points at key (base + sl/4), columns
-// 4 (sl%4) .. +3, and lane i receives column i of 4 consecutive keys.
-template <In PIN, int D>
-__device__ __forceinline__ void pv_accumulate(f32x16 (&acc)[D / 32], const uint32_t (&pk)[2][8],
-                                              const unsigned char* vl, int lane) {
+// O^T += V^T P^T for both row blocks over the 32 keys [32 hb, 32 hb + 32) of a
+// staged tile.  P^T (16-bit, B operand) is in the layout the S^T accumulator
+// left it: lane l holds query l%32 and, for k-step j0 in {0, 2}, keys
+// 32 hb + 8 j0 + {4 half + t, 8 + 4 half + t}, t < 4 (packed pairs
+// pk[2 j0 .. 2 j0 + 3]).  The matching V^T fragment (A operand: row d = l%32
+// of a 32-column block, the same 8 keys) is gathered with two transposing LDS
+// reads: within each 16-lane group, source lane sl points at key
+// base + sl/4, columns 4 (sl%4) .. +3, and lane i receives column i of the 4
+// consecutive keys.  Each fragment feeds both row blocks.
+template <In PIN, int D, int RB>
+__device__ __forceinline__ void pv_half(f32x16 (&acc)[RB][D / 32], const uint32_t (&pk)[RB][8],
+                                        const unsigned char* vl, int lane, int hb) {
   const int g = lane >> 4;          // 16-lane group
   const int sl = lane & 15;         // source lane within the group
+  // the fragment reads of each 8-key step are issued together, ahead of its
+  // MFMAs, so their latency is paid once per step rather than per MFMA
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
+  for (int j = 0; j < 2; ++j) {
+    uint4 aop[D / 32];
+    const int vrow = 32 * hb + 16 * j + 4 * (g >> 1) + (sl >> 2);
 #pragma unroll
-    for (int j0 = 0; j0 < 4; j0 += 2) {
-      const uint4 bop = make_uint4(pk[kb][2 * j0], pk[kb][2 * j0 + 1], pk[kb][2 * j0 + 2], pk[kb][2 * j0 + 3]);
-      const int kbase = 32 * kb + 8 * j0;
-      const int vrow = kbase + 4 * (g >> 1) + (sl >> 2);
-#pragma unroll
-      for (int c = 0; c < D / 32; ++c) {
-        const int dcol = 32 * c + 16 * (g & 1) + 4 * (sl & 3);
-        const int unit = dcol >> 3;
-        const int hoff = (dcol & 7) * 2;
-        const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)(vl + lds_offset<2 * D>(vrow, unit) + hoff));
-        const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)(vl + lds_offset<2 * D>(vrow + 8, unit) + hoff));
-        const uint2 w0 = __builtin_bit_cast(uint2, t0);
-        const uint2 w1 = __builtin_bit_cast(uint2, t1);
-        const uint4 aop = make_uint4(w0.x, w0.y, w1.x, w1.y);
-        acc[c] = mfma_16bit<PIN>(aop, bop, acc[c]);
-      }
+    for (int c = 0; c < D / 32; ++c) {
+      const int dcol = 32 * c + 16 * (g & 1) + 4 * (sl & 3);
+      const int unit = dcol >> 3;
+      const int hoff = (dcol & 7) * 2;
+      const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4*)(vl + lds_offset<2 * D>(vrow, unit) + hoff));
+      const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4*)(vl + lds_offset<2 * D>(vrow + 8, unit) + hoff));
+      const uint2 w0 = __builtin_bit_cast(uint2, t0);
+      const uint2 w1 = __builtin_bit_cast(uint2, t1);
+      aop[c] = make_uint4(w0.x, w0.y, w1.x, w1.y);
     }
+    uint4 bop[RB];
+#pragma unroll
+    for (int qb = 0; qb < RB; ++qb)
+      bop[qb] = make_uint4(pk[qb][4 * j], pk[qb][4 * j + 1], pk[qb][4 * j + 2], pk[qb][4 * j + 3]);
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+      for (int qb = 0; qb < RB; ++qb) acc[qb][c] = mfma_16bit<PIN>(aop[c], bop[qb], acc[qb][c]);
   }
 }
 
-template <In IN, int D>
+template <In IN, int D, int WAVES, int RB>
 struct Cfg {
   static constexpr bool kFp8 = (IN == In::FP8);
+  static constexpr int kThreads = 64 * WAVES;
+  static constexpr int kBM = 32 * RB * WAVES;        // query rows per workgroup
   static constexpr int kInBytes = kFp8 ? 1 : 2;
   static constexpr int kKRow = D * kInBytes;         // bytes per K row in LDS
   static constexpr int kVRow = D * 2;                // V is 16-bit in LDS
   static constexpr int kKTile = kBN * kKRow;
   static constexpr int kVTile = kBN * kVRow;
   static constexpr int kStage = kKTile + kVTile;
-  static constexpr int kLds = 2 * kStage;            // double buffered
   // fp8 V: 16-byte global chunks per thread per tile (register staged)
   static constexpr int kVPer = kBN * D * kInBytes / 16 / kThreads;
   static_assert(kFp8 ? (kBN * D * kInBytes / 16) % kThreads == 0 : true, "tile split");
-  static_assert(kKTile % (1024 * kWaves) == 0 && kVTile % (1024 * kWaves) == 0, "DMA split");
-  static constexpr int kQSteps = kFp8 ? D / 64 : D / 16;   // MFMA k-steps for S
+  static_assert(kKTile % (1024 * WAVES) == 0 && kVTile % (1024 * WAVES) == 0, "DMA split");
+  static constexpr int kQSteps = kFp8 ? D / 64 : D / 16;   // MFMA k-steps for S (per row block)
   static constexpr int kDBlocks = D / 32;                  // 32-wide output column blocks
 };
 
-template <In IN, int D>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <In IN, int D, int WAVES, int RB>
+__global__ void __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(3 - RB, 3 - RB)))
 attn_fwd_kernel(const FwdParams p) {
-  using C = Cfg<IN, D>;
+  using C = Cfg<IN, D, WAVES, RB>;
   constexpr In PIN = (IN == In::F16) ? In::F16 : In::BF16;   // type of P, V in LDS and O
-  // Two statically distinct stage buffers (K tile then V tile): the loop below
-  // is unrolled by two so that each half names its buffers at compile time,
-  // which lets the compiler keep the LDS DMA into one buffer in flight while
-  // the other one is read.
-  __shared__ __attribute__((aligned(1024))) unsigned char stage0[C::kStage];
-  __shared__ __attribute__((aligned(1024))) unsigned char stage1[C::kStage];
+  constexpr int kBM = C::kBM;
+  // Headroom (log2 units) of p above a row's reference max: 16-bit P holds
+  // 2^15 in fp16 (max 65504) and 2^64 in bf16 (max ~2^128).
+  constexpr float kGrowLimit = (PIN == In::F16) ? 15.0f : 64.0f;
+  // Two stage buffers (K tile then V tile) at fixed offsets of one LDS array:
+  // the loop below is unrolled by two so that each half names its buffer at
+  // compile time (one address register serves both, with an immediate
+  // offset), and the LDS DMA into one buffer stays in flight while the other
+  // one is read.
+  __shared__ __attribute__((aligned(1024))) unsigned char stages[2 * C::kStage];
+  unsigned char* const stage0 = stages;
+  unsigned char* const stage1 = stages + C::kStage;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, kept in an SGPR
   const int lane = tid & 63;
   const int half = lane >> 5;      // which 16 of each 32 keys this lane holds
-  const int col = lane & 31;       // the query row (within the wave) this lane owns
+  const int col = lane & 31;       // the query row (within each row block) this lane owns
 
-  // ---- work assignment: heaviest query tiles first; consecutive workgroups
-  // take consecutive (batch, head) pairs so one head stays on one XCD when
-  // B*H is a multiple of 8.
+  // ---- work assignment.  Workgroups are dealt to the 8 XCDs round-robin
+  // (workgroup i runs on XCD i % 8), each XCD with its own L2.  sched 1: XCD
+  // x serves heads x, x+8, x+16, ... one after another, all query tiles of a
+  // head back to back (heaviest first), so the tiles running together on an
+  // XCD read the same K/V through its L2.  sched 0 (or B*H not a multiple
+  // of 8): heaviest tiles of all heads first.
   const int bh_count = p.batch * p.heads;
-  const int tile = p.q_tiles - 1 - (int)(blockIdx.x / bh_count);
-  const int bh = (int)(blockIdx.x % bh_count);
+  int tile, bh;
+  if (p.sched == 1 && bh_count % 8 == 0) {
+    const int xcd = (int)(blockIdx.x % 8u);
+    const int slot = (int)(blockIdx.x / 8u);
+    tile = p.q_tiles - 1 - slot % p.q_tiles;
+    bh = xcd + 8 * (slot / p.q_tiles);
+  } else {
+    tile = p.q_tiles - 1 - (int)(blockIdx.x / bh_count);
+    bh = (int)(blockIdx.x % bh_count);
+  }
   const int b = bh / p.heads;
   const int h = bh - b * p.heads;
   const int q0 = tile * kBM;
@@ -268,25 +299,32 @@ attn_fwd_kernel(const FwdParams p) {
   const int kt_begin = kr.lo / kBN;
   const int kt_end = (kr.hi + kBN - 1) / kBN;
 
+  // ---- this wave's rows: RB blocks of 32, lane `col` owns one row in each
+  const int wr0 = q0 + wave * 32 * RB;     // first row of the wave
+  const int wr1 = min(wr0 + 32 * RB, n);   // one past its last real row
+  int qrow[RB];
+#pragma unroll
+  for (int qb = 0; qb < RB; ++qb) qrow[qb] = wr0 + 32 * qb + col;
+
   // ---- Q^T fragments (B operand), kept in registers for the whole kernel.
-  const int qrow = q0 + wave * 32 + col;
-  uint4 qf[C::kFp8 ? 2 * C::kQSteps : C::kQSteps];
-  {
-    const bool ok = qrow < n;
-    const unsigned char* src = qg + (int64_t)(ok ? qrow : 0) * p.q_ss * C::kInBytes;
+  uint4 qf[RB][C::kFp8 ? 2 * C::kQSteps : C::kQSteps];
+#pragma unroll
+  for (int qb = 0; qb < RB; ++qb) {
+    const bool ok = qrow[qb] < n;
+    const unsigned char* src = qg + (int64_t)(ok ? qrow[qb] : 0) * p.q_ss * C::kInBytes;
     if constexpr (C::kFp8) {
 #pragma unroll
       for (int st = 0; st < C::kQSteps; ++st) {
         // lane holds d = 64 st + 32 half + [0, 32): two 16-byte pieces
         const uint4* g = (const uint4*)(src + 64 * st + 32 * half);
-        qf[2 * st] = ok ? g[0] : make_uint4(0, 0, 0, 0);
-        qf[2 * st + 1] = ok ? g[1] : make_uint4(0, 0, 0, 0);
+        qf[qb][2 * st] = ok ? g[0] : make_uint4(0, 0, 0, 0);
+        qf[qb][2 * st + 1] = ok ? g[1] : make_uint4(0, 0, 0, 0);
       }
     } else {
 #pragma unroll
       for (int st = 0; st < C::kQSteps; ++st) {
         // lane holds d = 16 st + 8 half + [0, 8)
-        qf[st] = ok ? *(const uint4*)(src + (16 * st + 8 * half) * 2) : make_uint4(0, 0, 0, 0);
+        qf[qb][st] = ok ? *(const uint4*)(src + (16 * st + 8 * half) * 2) : make_uint4(0, 0, 0, 0);
       }
     }
   }
@@ -295,53 +333,67 @@ attn_fwd_kernel(const FwdParams p) {
   // 16-bit K and V, and fp8 K, go straight from global memory to LDS
   // (global_load_lds_dwordx4): one wave instruction fills 1 KB of LDS, lane L
   // writing 16-byte unit L of it, so each lane fetches the global unit that
-  // the swizzle maps to that LDS position.  Keys past the end are clamped to
-  // the last key; those keys are masked (p = 0) in the boundary tile.
+  // the swizzle maps to that LDS position.  In the last tile, keys past the
+  // end are clamped to the last key; those keys are masked (p = 0).
   // fp8 V goes through registers and is widened to bf16 on the way into LDS.
-  constexpr int kKBlocks = C::kKTile / 1024 / kWaves;      // DMA instructions per wave, K
-  constexpr int kVBlocks = C::kFp8 ? 0 : C::kVTile / 1024 / kWaves;
-  int k_row[kKBlocks], k_col[kKBlocks];                    // tile row and byte column per DMA
-  int v_row[kVBlocks > 0 ? kVBlocks : 1], v_col[kVBlocks > 0 ? kVBlocks : 1];
-#pragma unroll
-  for (int i = 0; i < kKBlocks; ++i) {
-    const int pos = (wave * kKBlocks + i) * 64 + lane;       // physical unit in the tile
-    k_row[i] = pos / (C::kKRow / 16);
-    k_col[i] = (swizzled_unit<C::kKRow>(k_row[i], pos % (C::kKRow / 16))) * 16;
-  }
-#pragma unroll
-  for (int i = 0; i < kVBlocks; ++i) {
-    const int pos = (wave * kVBlocks + i) * 64 + lane;
-    v_row[i] = pos / (C::kVRow / 16);
-    v_col[i] = (swizzled_unit<C::kVRow>(v_row[i], pos % (C::kVRow / 16))) * 16;
-  }
+  constexpr int kKBlocks = C::kKTile / 1024 / WAVES;     // DMA instructions per wave, K
+  constexpr int kVBlocks = C::kFp8 ? 0 : C::kVTile / 1024 / WAVES;
+  constexpr int kVB = kVBlocks > 0 ? kVBlocks : 1;
+  // Tile row and byte column of the unit lane `lane` fetches in DMA block `blk`.
+  auto dma_row = [&](int blk, int row_bytes) { return (blk * 64 + lane) / (row_bytes / 16); };
+  auto dma_col = [&](int blk, int row_bytes) {
+    const int pos = blk * 64 + lane;
+    const int row = pos / (row_bytes / 16);
+    const int phys = pos % (row_bytes / 16);
+    return (row_bytes == 256 ? swizzled_unit<256>(row, phys) : swizzled_unit<128>(row, phys)) * 16;
+  };
+  // Byte offset, from the tile's first key, of the unit this lane fetches in
+  // DMA block `blk` (recomputed per tile: cheaper than keeping it live).
+  auto k_off = [&](int i) {
+    const int blk = wave * kKBlocks + i;
+    return (uint32_t)(dma_row(blk, C::kKRow) * k_row_stride + dma_col(blk, C::kKRow));
+  };
+  auto v_off = [&](int i) {
+    const int blk = wave * kVBlocks + i;
+    return (uint32_t)(dma_row(blk, C::kVRow) * v_row_stride + dma_col(blk, C::kVRow));
+  };
   uint4 vreg[C::kFp8 ? C::kVPer : 1];
   auto issue_tile = [&](int kt, unsigned char* dst) {
     const int k0 = kt * kBN;
-    const int last = n - 1 - k0;                             // clamp rows past the end
+    const int last = n - 1 - k0;                               // last valid row of this tile
     const unsigned char* kb_ = kg + (int64_t)k0 * k_row_stride;
+    const unsigned char* vb_ = vg + (int64_t)k0 * v_row_stride;
+    if (last >= kBN - 1) {
 #pragma unroll
-    for (int i = 0; i < kKBlocks; ++i) {
-      const int r = min(k_row[i], last);
-      __builtin_amdgcn_global_load_lds((const void*)(kb_ + r * k_row_stride + k_col[i]),
-                                       (__attribute__((address_space(3))) void*)(dst + (wave * kKBlocks + i) * 1024),
-                                       16, 0, 0);
-    }
-    if constexpr (!C::kFp8) {
-      const unsigned char* vb_ = vg + (int64_t)k0 * v_row_stride;
+      for (int i = 0; i < kKBlocks; ++i)
+        __builtin_amdgcn_global_load_lds((const void*)(kb_ + k_off(i)),
+                                         (__attribute__((address_space(3))) void*)(dst + (wave * kKBlocks + i) * 1024),
+                                         16, 0, 0);
 #pragma unroll
-      for (int i = 0; i < kVBlocks; ++i) {
-        const int r = min(v_row[i], last);
+      for (int i = 0; i < kVBlocks; ++i)
         __builtin_amdgcn_global_load_lds(
-            (const void*)(vb_ + r * v_row_stride + v_col[i]),
+            (const void*)(vb_ + v_off(i)),
             (__attribute__((address_space(3))) void*)(dst + C::kKTile + (wave * kVBlocks + i) * 1024), 16, 0, 0);
-      }
     } else {
-      const unsigned char* vb_ = vg + (int64_t)k0 * v_row_stride;
+#pragma unroll
+      for (int i = 0; i < kKBlocks; ++i)
+        __builtin_amdgcn_global_load_lds(
+            (const void*)(kb_ + (uint32_t)(min(dma_row(wave * kKBlocks + i, C::kKRow), last) * k_row_stride +
+                                           dma_col(wave * kKBlocks + i, C::kKRow))),
+            (__attribute__((address_space(3))) void*)(dst + (wave * kKBlocks + i) * 1024), 16, 0, 0);
+#pragma unroll
+      for (int i = 0; i < kVBlocks; ++i)
+        __builtin_amdgcn_global_load_lds(
+            (const void*)(vb_ + (uint32_t)(min(dma_row(wave * kVBlocks + i, C::kVRow), last) * v_row_stride +
+                                           dma_col(wave * kVBlocks + i, C::kVRow))),
+            (__attribute__((address_space(3))) void*)(dst + C::kKTile + (wave * kVBlocks + i) * 1024), 16, 0, 0);
+    }
+    if constexpr (C::kFp8) {
 #pragma unroll
       for (int i = 0; i < C::kVPer; ++i) {
-        const int id = tid + i * kThreads;
+        const int id = tid + i * C::kThreads;
         const int r = min(id / (D / 16), last);
-        vreg[i] = *(const uint4*)(vb_ + r * v_row_stride + (id % (D / 16)) * 16);
+        vreg[i] = *(const uint4*)(vb_ + (uint32_t)(r * v_row_stride + (id % (D / 16)) * 16));
       }
     }
   };
@@ -351,7 +403,7 @@ attn_fwd_kernel(const FwdParams p) {
       unsigned char* vl = dst + C::kKTile;
 #pragma unroll
       for (int i = 0; i < C::kVPer; ++i) {
-        const int id = tid + i * kThreads;
+        const int id = tid + i * C::kThreads;
         const int row = id / (D / 16);           // 16 fp8 per global chunk
         const int unit = (id % (D / 16)) * 2;    // two 16-byte bf16 units
         uint4 lo, hi;
@@ -362,156 +414,273 @@ attn_fwd_kernel(const FwdParams p) {
     }
   };
 
-  // ---- running state
-  f32x16 acc[C::kDBlocks];
+  // ---- running state, per row block
+  f32x16 acc[RB][C::kDBlocks];
 #pragma unroll
-  for (int c = 0; c < C::kDBlocks; ++c)
+  for (int qb = 0; qb < RB; ++qb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[c][r] = 0.f;
-  float m_run = -INFINITY;     // reference max of the raw (unscaled) scores
-  float neg_mc = 0.f;          // -m_run * c, or 0 while no key was seen
-  float l_part = 0.f;          // this lane's share of the row sum
-  const float cexp = p.c_log2;  // softmax scale * log2(e) (* fp8 descales)
+    for (int c = 0; c < C::kDBlocks; ++c)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[qb][c][r] = 0.f;
+  float m_run[RB], neg_mc[RB], l_part[RB], m_max[RB];
+#pragma unroll
+  for (int qb = 0; qb < RB; ++qb) {
+    m_run[qb] = -INFINITY;   // reference max of the raw (unscaled) scores
+    neg_mc[qb] = 0.f;        // -m_run * c, or 0 while no key was seen
+    l_part[qb] = 0.f;        // this lane's share of the row sum
+    m_max[qb] = -INFINITY;   // exact running max of the raw scores
+  }
+  bool redo = false;                          // a row outgrew its reference (see fold_max)
+  const float cexp = p.c_log2;                 // softmax scale * log2(e) (* fp8 descales)
+  // Keys visible from each of this lane's rows form one interval [vis_lo, vis_hi].
+  int vis_lo[RB];
+  uint32_t vis_span[RB];
+#pragma unroll
+  for (int qb = 0; qb < RB; ++qb) {
+    const int qi = qrow[qb];
+    vis_lo[qb] = p.wl >= 0 ? qi - p.wl : 0;
+    int hi = n - 1;
+    if (p.causal) hi = min(hi, qi);
+    if (p.wr >= 0) hi = min(hi, qi + p.wr);
+    vis_span[qb] = (uint32_t)(hi - vis_lo[qb]);
+  }
 
-  const int wr0 = q0 + wave * 32;          // this wave's first row
-  const int wr1 = min(wr0 + 32, n);        // one past its last real row
+  // ---- building blocks over 32-key halves of a staged tile ----------------
+  // S^T for keys [32 hb, 32 hb + 32) of the tile whose K part is at `kl`, for
+  // both row blocks (each K fragment feeds two MFMAs).
+  auto s_half = [&](const unsigned char* kl, int hb, f32x16 (&s)[RB]) {
+#pragma unroll
+    for (int qb = 0; qb < RB; ++qb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[qb][r] = 0.f;
+    const int krow = 32 * hb + col;
+    if constexpr (C::kFp8) {
+      uint4 a[2 * C::kQSteps];
+#pragma unroll
+      for (int st = 0; st < C::kQSteps; ++st) {
+        const int u0 = (64 * st + 32 * half) / 16;
+        a[2 * st] = *(const uint4*)(kl + lds_offset<C::kKRow>(krow, u0));
+        a[2 * st + 1] = *(const uint4*)(kl + lds_offset<C::kKRow>(krow, u0 + 1));
+      }
+#pragma unroll
+      for (int st = 0; st < C::kQSteps; ++st)
+#pragma unroll
+        for (int qb = 0; qb < RB; ++qb) s[qb] = mfma_fp8(a[2 * st], a[2 * st + 1], qf[qb][2 * st], qf[qb][2 * st + 1], s[qb]);
+    } else {
+      // K fragment reads are issued in groups ahead of their MFMAs, so their
+      // latency is paid once per group rather than per MFMA
+      constexpr int kGroup = 4;
+#pragma unroll
+      for (int st0 = 0; st0 < C::kQSteps; st0 += kGroup) {
+        uint4 a[kGroup];
+#pragma unroll
+        for (int j = 0; j < kGroup; ++j) a[j] = *(const uint4*)(kl + lds_offset<C::kKRow>(krow, 2 * (st0 + j) + half));
+#pragma unroll
+        for (int j = 0; j < kGroup; ++j)
+#pragma unroll
+          for (int qb = 0; qb < RB; ++qb) s[qb] = mfma_16bit<IN>(a[j], qf[qb][st0 + j], s[qb]);
+      }
+    }
+  };
+  auto block_max = [](const f32x16& x) {
+    float m = x[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) m = fmaxf(m, x[r]);
+    return m;
+  };
+  // Fold a block's row maxima into the running state.  A row's reference max
+  // is fixed at the first block where it sees a key (O and l are still zero
+  // then, so nothing needs rescaling) and never moves afterwards: p may then
+  // exceed 1, up to 2^kGrowLimit, which the 16-bit P format and the fp32
+  // sums hold without overflow and with unchanged relative precision.  A row
+  // whose scores climb further sets `redo`; the workgroup then repeats the
+  // key loop with the exact row maximum (tracked in m_max) as reference.
+  auto fold_max = [&](const float (&mt)[RB]) {
+#pragma unroll
+    for (int qb = 0; qb < RB; ++qb) {
+      const float m = pair_max(mt[qb]);
+      m_max[qb] = fmaxf(m_max[qb], m);
+      if (m_run[qb] == -INFINITY) {
+        m_run[qb] = m;
+        neg_mc[qb] = (m == -INFINITY) ? 0.f : -m * cexp;
+      } else {
+        redo = redo || ((m - m_run[qb]) * cexp > kGrowLimit);
+      }
+    }
+  };
+  // p = exp2(s c - m c) for a 32-key half of both row blocks, packed to 16
+  // bits; the row sum takes the unrounded fp32 p.
+  auto exp_pack = [&](const f32x16 (&s)[RB], uint32_t (&pk)[RB][8]) {
+#pragma unroll
+    for (int qb = 0; qb < RB; ++qb)
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][2 * r], cexp, neg_mc[qb]));
+        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][2 * r + 1], cexp, neg_mc[qb]));
+        l_part[qb] += e0;
+        l_part[qb] += e1;
+        pk[qb][r] = pack2<PIN>(e0, e1);
+      }
+  };
+  // The 16-bit rounding residual p - round16(p) of a half packed by exp_pack
+  // with the same reference, itself packed to 16 bits.
+  auto residual = [&](const f32x16 (&s)[RB], const uint32_t (&pk)[RB][8], uint32_t (&pr)[RB][8]) {
+#pragma unroll
+    for (int qb = 0; qb < RB; ++qb)
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][2 * r], cexp, neg_mc[qb]));
+        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][2 * r + 1], cexp, neg_mc[qb]));
+        pr[qb][r] = pack2<PIN>(e0 - unpack_lo<PIN>(pk[qb][r]), e1 - unpack_hi<PIN>(pk[qb][r]));
+      }
+  };
+  // Mask a 32-key half: key k0 + 32 hb + 8 (r/4) + 4 half + (r%4).
+  auto apply_mask = [&](f32x16 (&s)[RB], int k0, int hb) {
+#pragma unroll
+    for (int qb = 0; qb < RB; ++qb) {
+      const int base = k0 + 32 * hb + 4 * half - vis_lo[qb];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const uint32_t rel = (uint32_t)(base + 8 * (r >> 2) + (r & 3));
+        if (rel > vis_span[qb]) s[qb][r] = -INFINITY;
+      }
+    }
+  };
 
-  // One K/V tile of work for this wave, reading the tile staged in `cur`.
-  auto compute_tile = [&](int kt, const unsigned char* cur) {
+  // ---- one tile: software-pipelined halves a (keys 0-31), b (32-63).
+  // `masked` (wave-uniform): the tile crosses a mask edge or the sequence
+  // end.  Its scores are masked, and the 16-bit rounding residual of p goes
+  // through a second P.V pass -- these tiles hold the rows with few visible
+  // keys, where the rounding of p does not average out.
+  constexpr int kSMfma = RB * C::kQSteps;            // S MFMAs per half (all row blocks)
+  constexpr int kPVMfma = RB * 2 * C::kDBlocks;      // P.V MFMAs per half
+  constexpr int kExpValu = RB * 56;                  // softmax VALU per half (all row blocks)
+  auto compute_tile = [&](int kt, const unsigned char* cur, bool masked) {
     const int k0 = kt * kBN;
     const unsigned char* kl = cur;
     const unsigned char* vl = cur + C::kKTile;
-    if (block_none_visible(wr0, wr1, k0, k0 + kBN, n, p.causal, p.wl, p.wr)) return;
-    const bool masked = !block_all_visible(wr0, wr1, k0, k0 + kBN, n, p.causal, p.wl, p.wr);
-    // ---- S^T = K Q^T for the 64 keys: two 32x32 blocks
-    f32x16 s[2];
+    f32x16 sa[RB], sb[RB];
+    uint32_t pa[RB][8], pb[RB][8];
+    s_half(kl, 0, sa);
+    if (masked) apply_mask(sa, k0, 0);
+    {
+      float mt[RB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-      const int krow = 32 * kb + col;
-      if constexpr (C::kFp8) {
-#pragma unroll
-        for (int st = 0; st < C::kQSteps; ++st) {
-          const int u0 = (64 * st + 32 * half) / 16;
-          const uint4 a0 = *(const uint4*)(kl + lds_offset<C::kKRow>(krow, u0));
-          const uint4 a1 = *(const uint4*)(kl + lds_offset<C::kKRow>(krow, u0 + 1));
-          i32x8 av = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-          const uint4 b0 = qf[2 * st], b1 = qf[2 * st + 1];
-          i32x8 bv = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
-          s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, s[kb], 0, 0, 0, 127, 0, 127);
-        }
-      } else {
-#pragma unroll
-        for (int st = 0; st < C::kQSteps; ++st) {
-          const uint4 a = *(const uint4*)(kl + lds_offset<C::kKRow>(krow, 2 * st + half));
-          s[kb] = mfma_16bit<IN>(a, qf[st], s[kb]);
-        }
-      }
+      for (int qb = 0; qb < RB; ++qb) mt[qb] = block_max(sa[qb]);
+      fold_max(mt);
     }
-    // ---- mask (boundary tiles only)
+    __builtin_amdgcn_sched_barrier(0);
+    s_half(kl, 1, sb);
+    exp_pack(sa, pa);
+#pragma unroll
+    for (int i = 0; i < kSMfma; ++i) {
+      if (i % (4 * RB) == 0) __builtin_amdgcn_sched_group_barrier(0x100, C::kFp8 ? 2 * C::kQSteps : 4, 0);  // K reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                  // S_b MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, kExpValu / kSMfma, 0);                  // softmax VALU
+    }
+    __builtin_amdgcn_sched_barrier(0);
     if (masked) {
-      const int qi = wr0 + col;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kj = k0 + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
-          bool vis = kj < n;
-          if (p.causal) vis = vis && (kj <= qi);
-          if (p.wl >= 0) vis = vis && (kj >= qi - p.wl);
-          if (p.wr >= 0) vis = vis && (kj <= qi + p.wr);
-          if (!vis) s[kb][r] = -INFINITY;
-        }
+      apply_mask(sb, k0, 1);
+      uint32_t ra[RB][8];
+      residual(sa, pa, ra);              // same reference as pa: before the next fold
+      pv_half<PIN, D, RB>(acc, ra, vl, lane, 0);
     }
-    // ---- online softmax
-    float mt = s[0][0];
+    {
+      float mt[RB];
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mt = fmaxf(mt, s[0][r]);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[1][r]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float m_new = fmaxf(m_run, mt);
-    const bool grow = (m_new != -INFINITY) && (m_run == -INFINITY || (m_new - m_run) * cexp > kRescaleThreshold);
-    if (__ballot(grow) != 0ull) {
-      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f((m_run - m_new) * cexp);
-      m_run = m_new;
-      neg_mc = (m_run == -INFINITY) ? 0.f : -m_run * cexp;
-      l_part *= alpha;
-#pragma unroll
-      for (int c = 0; c < C::kDBlocks; ++c)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[c][r] *= alpha;
+      for (int qb = 0; qb < RB; ++qb) mt[qb] = block_max(sb[qb]);
+      fold_max(mt);
     }
-    // p = exp2(s c - m c); the row sum uses the unrounded fp32 p.
-    float e[2][16];
+    __builtin_amdgcn_sched_barrier(0);
+    pv_half<PIN, D, RB>(acc, pa, vl, lane, 0);
+    exp_pack(sb, pb);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        e[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], cexp, neg_mc));
-        l_part += e[kb][r];
-      }
-    uint32_t pk[2][8], pr[2][8];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        pk[kb][r] = pack2<PIN>(e[kb][2 * r], e[kb][2 * r + 1]);
-        // Boundary tiles carry the rows with few visible keys, where the
-        // 16-bit rounding of p does not average out: there the rounding
-        // residual p - round16(p) goes through a second P.V pass.
-        if (masked)
-          pr[kb][r] = pack2<PIN>(e[kb][2 * r] - unpack_lo<PIN>(pk[kb][r]), e[kb][2 * r + 1] - unpack_hi<PIN>(pk[kb][r]));
-      }
-    pv_accumulate<PIN, D>(acc, pk, vl, lane);
-    if (masked) pv_accumulate<PIN, D>(acc, pr, vl, lane);
+    for (int i = 0; i < kPVMfma; ++i) {
+      if (i % (RB * C::kDBlocks) == 0) __builtin_amdgcn_sched_group_barrier(0x100, 2 * C::kDBlocks, 0);  // V^T reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                  // P_a.V MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, kExpValu / kPVMfma, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    pv_half<PIN, D, RB>(acc, pb, vl, lane, 1);
+    if (masked) {
+      uint32_t rb[RB][8];
+      residual(sb, pb, rb);
+      pv_half<PIN, D, RB>(acc, rb, vl, lane, 1);
+    }
+  };
+
+  auto tile_step = [&](int kt, const unsigned char* cur) {
+    const int k0 = kt * kBN;
+    if (block_none_visible(wr0, wr1, k0, k0 + kBN, n, p.causal, p.wl, p.wr)) return;
+    compute_tile(kt, cur, !block_all_visible(wr0, wr1, k0, k0 + kBN, n, p.causal, p.wl, p.wr));
   };
 
   // ---- main loop: tile kt is read from one stage while tile kt+1 lands in
   // the other.  Each barrier publishes the next tile (its DMA must have
-  // landed, hence the full wait) and frees the stage just read.
-  if (kt_begin < kt_end) {
-    issue_tile(kt_begin, stage0);
-    store_v_fp8(stage0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    int kt = kt_begin;
-    while (true) {
-      issue_tile(min(kt + 1, kt_end - 1), stage1);
-      compute_tile(kt, stage0);
-      store_v_fp8(stage1);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      if (++kt == kt_end) break;
-      issue_tile(min(kt + 1, kt_end - 1), stage0);
-      compute_tile(kt, stage1);
+  // landed, hence the full wait) and frees the stage just read.  A second
+  // pass runs only if some row outgrew its reference (see fold_max).
+  for (int pass = 0; pass < 2; ++pass) {
+    if (kt_begin < kt_end) {
+      issue_tile(kt_begin, stage0);
       store_v_fp8(stage0);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      if (++kt == kt_end) break;
+      int kt = kt_begin;
+      while (true) {
+        issue_tile(min(kt + 1, kt_end - 1), stage1);
+        tile_step(kt, stage0);
+        store_v_fp8(stage1);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (++kt == kt_end) break;
+        issue_tile(min(kt + 1, kt_end - 1), stage0);
+        tile_step(kt, stage1);
+        store_v_fp8(stage0);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (++kt == kt_end) break;
+      }
     }
+    if (pass == 1 || !__syncthreads_or(redo ? 1 : 0)) break;
+    // restart every row of the workgroup from its exact maximum
+#pragma unroll
+    for (int qb = 0; qb < RB; ++qb) {
+      m_run[qb] = m_max[qb];
+      neg_mc[qb] = (m_max[qb] == -INFINITY) ? 0.f : -m_max[qb] * cexp;
+      l_part[qb] = 0.f;
+#pragma unroll
+      for (int c = 0; c < C::kDBlocks; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[qb][c][r] = 0.f;
+    }
+    redo = false;
   }
 
   // ---- epilogue: O = O_acc / l (* v descale), LSE = ln(2) * (m c + log2 l)
-  const float l_row = l_part + __shfl_xor(l_part, 32);
-  if (qrow < n) {
-    const float inv = l_row > 0.f ? p.v_descale / l_row : 0.f;
-    constexpr int kOutBytes = 2;
-    unsigned char* og = (unsigned char*)p.o + ((int64_t)b * p.o_sb + (int64_t)h * p.o_sh + (int64_t)qrow * p.o_ss) * kOutBytes;
 #pragma unroll
-    for (int c = 0; c < C::kDBlocks; ++c)
+  for (int qb = 0; qb < RB; ++qb) {
+    const float l_row = l_part[qb] + __shfl_xor(l_part[qb], 32);
+    if (qrow[qb] < n) {
+      const float inv = l_row > 0.f ? p.v_descale / l_row : 0.f;
+      constexpr int kOutBytes = 2;
+      unsigned char* og = (unsigned char*)p.o +
+                          ((int64_t)b * p.o_sb + (int64_t)h * p.o_sh + (int64_t)qrow[qb] * p.o_ss) * kOutBytes;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int d = 32 * c + 8 * j + 4 * half;
-        store4<PIN>(og + d * kOutBytes, acc[c][4 * j] * inv, acc[c][4 * j + 1] * inv, acc[c][4 * j + 2] * inv,
-                    acc[c][4 * j + 3] * inv);
+      for (int c = 0; c < C::kDBlocks; ++c)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int d = 32 * c + 8 * j + 4 * half;
+          uint2 w;
+          w.x = pack2<PIN>(acc[qb][c][4 * j] * inv, acc[qb][c][4 * j + 1] * inv);
+          w.y = pack2<PIN>(acc[qb][c][4 * j + 2] * inv, acc[qb][c][4 * j + 3] * inv);
+          *(uint2*)(og + d * kOutBytes) = w;
+        }
+      if (p.lse != nullptr && half == 0) {
+        const float lse = (m_run[qb] == -INFINITY || !(l_row > 0.f))
+                              ? -INFINITY
+                              : (m_run[qb] * cexp + __builtin_amdgcn_logf(l_row)) * kLn2;
+        p.lse[(int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh + qrow[qb]] = lse;
       }
-    if (p.lse != nullptr && half == 0) {
-      const float lse = (m_run == -INFINITY || !(l_row > 0.f))
-                            ? -INFINITY
-                            : (m_run * cexp + __builtin_amdgcn_logf(l_row)) * kLn2;
-      p.lse[(int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh + qrow] = lse;
     }
   }
 }
@@ -519,18 +688,19 @@ attn_fwd_kernel(const FwdParams p) {
 // ---------------------------------------------------------------------------
 // Host-side launch
 // ---------------------------------------------------------------------------
-template <In IN, int D>
+template <In IN, int D, int WAVES, int RB>
 static hipError_t launch_t(const FwdParams& p, hipStream_t stream) {
-  using C = Cfg<IN, D>;
   const dim3 grid((unsigned)((int64_t)p.q_tiles * p.batch * p.heads));
-  const dim3 block(kThreads);
-  hipLaunchKernelGGL((attn_fwd_kernel<IN, D>), grid, block, 0, stream, p);
+  const dim3 block(64 * WAVES);
+  hipLaunchKernelGGL((attn_fwd_kernel<IN, D, WAVES, RB>), grid, block, 0, stream, p);
   return hipGetLastError();
 }
 
-int tile_bm() { return kBM; }
+// Tile configurations: 0 = 128 query rows (4 waves x 32 rows, two waves per
+// SIMD), 1 = 256 query rows (4 waves x 64 rows, one wave per SIMD).
+int tile_bm(int cfg) { return cfg == 1 ? 256 : 128; }
+int tile_waves(int /*cfg*/) { return 4; }
 int tile_bn() { return kBN; }
-int tile_waves() { return kWaves; }
 
 int lds_bytes(int in_dtype, int d) {
   const bool fp8 = in_dtype == 3;
@@ -538,25 +708,33 @@ int lds_bytes(int in_dtype, int d) {
   return 2 * (kBN * d * kin + kBN * d * 2);
 }
 
-hipError_t launch_fwd(const FwdParams& p, int in_dtype, int d, hipStream_t stream) {
-  // in_dtype: 1 = f16, 2 = bf16, 3 = fp8 e4m3 (validated by the caller)
-  if (in_dtype == 1 && d == 64) return launch_t<In::F16, 64>(p, stream);
-  if (in_dtype == 1 && d == 128) return launch_t<In::F16, 128>(p, stream);
-  if (in_dtype == 2 && d == 64) return launch_t<In::BF16, 64>(p, stream);
-  if (in_dtype == 2 && d == 128) return launch_t<In::BF16, 128>(p, stream);
-  if (in_dtype == 3 && d == 128) return launch_t<In::FP8, 128>(p, stream);
+template <int RB>
+static hipError_t launch_cfg(const FwdParams& p, int in_dtype, int d, hipStream_t stream) {
+  if (in_dtype == 1 && d == 64) return launch_t<In::F16, 64, 4, RB>(p, stream);
+  if (in_dtype == 1 && d == 128) return launch_t<In::F16, 128, 4, RB>(p, stream);
+  if (in_dtype == 2 && d == 64) return launch_t<In::BF16, 64, 4, RB>(p, stream);
+  if (in_dtype == 2 && d == 128) return launch_t<In::BF16, 128, 4, RB>(p, stream);
+  if (in_dtype == 3 && d == 128) return launch_t<In::FP8, 128, 4, RB>(p, stream);
   return hipErrorInvalidValue;
 }
 
-const char* kernel_name(int in_dtype, int d) {
-  switch (in_dtype * 1000 + d) {
-    case 1064: return "attn_fwd<f16,d64,bm128,bn64>";
-    case 1128: return "attn_fwd<f16,d128,bm128,bn64>";
-    case 2064: return "attn_fwd<bf16,d64,bm128,bn64>";
-    case 2128: return "attn_fwd<bf16,d128,bm128,bn64>";
-    case 3128: return "attn_fwd<fp8,d128,bm128,bn64>";
-    default: return "none";
-  }
+hipError_t launch_fwd(const FwdParams& p, int in_dtype, int d, int cfg, hipStream_t stream) {
+  // in_dtype: 1 = f16, 2 = bf16, 3 = fp8 e4m3 (validated by the caller)
+  if (cfg == 0) return launch_cfg<1>(p, in_dtype, d, stream);
+  if (cfg == 1) return launch_cfg<2>(p, in_dtype, d, stream);
+  return hipErrorInvalidValue;
+}
+
+const char* kernel_name(int in_dtype, int d, int cfg) {
+  static const char* names[2][3][2] = {
+      {{"attn_fwd<f16,d64,bm128,bn64>", "attn_fwd<f16,d128,bm128,bn64>"},
+       {"attn_fwd<bf16,d64,bm128,bn64>", "attn_fwd<bf16,d128,bm128,bn64>"},
+       {"none", "attn_fwd<fp8,d128,bm128,bn64>"}},
+      {{"attn_fwd<f16,d64,bm256,bn64>", "attn_fwd<f16,d128,bm256,bn64>"},
+       {"attn_fwd<bf16,d64,bm256,bn64>", "attn_fwd<bf16,d128,bm256,bn64>"},
+       {"none", "attn_fwd<fp8,d128,bm256,bn64>"}}};
+  if (in_dtype < 1 || in_dtype > 3 || (d != 64 && d != 128) || (cfg != 0 && cfg != 1)) return "none";
+  return names[cfg][in_dtype - 1][d == 128];
 }
 
 }  // namespace ea

@@ -90,10 +90,20 @@ def test_plan_valid_configs():
         for layout in ("bshd", "bhsd"):
             st, info = plan_status(make(dtype=dtype, D=D, layout=layout))
             assert st == _lib.EA_OK, _lib.status_string(st)
+            # four waves of 32 query rows per workgroup
             assert info.block_m == 128 and info.block_n == 64 and info.waves == 4
             assert info.grid == 2 * 3 * math.ceil(300 / 128)
             assert info.kernel.decode().startswith("attn_fwd<")
             assert info.lds_bytes <= 160 * 1024
+
+
+def test_plan_headline_shape():
+    st, info = plan_status(make(B=4, N=4096, H=32, causal=1))
+    assert st == 0 and info.waves == 4 and info.block_m == 128
+    assert info.grid == 4 * 32 * 32
+    # causal: query tile t (128 rows) visits 2t+2 key tiles of 64, 2 of them on the diagonal
+    assert info.kv_tiles == 128 * sum(2 * t + 2 for t in range(32))
+    assert info.masked_tiles == 128 * 32 * 2
 
 
 def test_plan_tile_counts_causal_and_window():

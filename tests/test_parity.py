@@ -88,3 +88,22 @@ def test_workload_sampled(name):
     r = sampled_check(inp, w.dtype, o, lse, heads, rows, causal=w.causal, window=window, scale=w.softmax_scale,
                       layout=w.layout, what=name)
     print(name, r)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_scores_outgrowing_the_first_tile(dtype, causal):
+    # Keys grow along the sequence, so late scores exceed the first tile's
+    # maximum by far more than the 16-bit P headroom: the kernel's second pass
+    # (exact row maximum as reference) must produce the right result.
+    import torch as _t
+    from exact_attention_04_amd.workloads import Inputs, torch_dtype
+    n, d = 700, 64
+    rng = np.random.default_rng(31)
+    q = np.ones((1, n, 2, d), dtype=np.float32) + 0.1 * rng.standard_normal((1, n, 2, d)).astype(np.float32)
+    ramp = (np.arange(n, dtype=np.float32) / n)[None, :, None, None]
+    k = ramp * (1.0 + 0.1 * rng.standard_normal((1, n, 2, d)).astype(np.float32))
+    v = rng.standard_normal((1, n, 2, d)).astype(np.float32)
+    td = torch_dtype(dtype)
+    inp = Inputs(*(_t.from_numpy(x).to(td) for x in (q, k, v)), (1.0, 1.0, 1.0))
+    full_check(inp, dtype, causal=causal, scale=1.0, what=f"growing scores {dtype} causal={causal}")
