@@ -249,9 +249,6 @@ attn_fwd_kernel(const FwdParams p) {
   using C = Cfg<IN, D, WAVES, RB>;
   constexpr In PIN = (IN == In::F16) ? In::F16 : In::BF16;   // type of P, V in LDS and O
   constexpr int kBM = C::kBM;
-  // Headroom (log2 units) of p above a row's reference max: 16-bit P holds
-  // 2^15 in fp16 (max 65504) and 2^64 in bf16 (max ~2^128).
-  constexpr float kGrowLimit = (PIN == In::F16) ? 15.0f : 64.0f;
   // Two stage buffers (K tile then V tile) at fixed offsets of one LDS array:
   // the loop below is unrolled by two so that each half names its buffer at
   // compile time (one address register serves both, with an immediate
@@ -422,15 +419,13 @@ attn_fwd_kernel(const FwdParams p) {
     for (int c = 0; c < C::kDBlocks; ++c)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[qb][c][r] = 0.f;
-  float m_run[RB], neg_mc[RB], l_part[RB], m_max[RB];
+  float m_run[RB], neg_mc[RB], l_part[RB];
 #pragma unroll
   for (int qb = 0; qb < RB; ++qb) {
     m_run[qb] = -INFINITY;   // reference max of the raw (unscaled) scores
     neg_mc[qb] = 0.f;        // -m_run * c, or 0 while no key was seen
     l_part[qb] = 0.f;        // this lane's share of the row sum
-    m_max[qb] = -INFINITY;   // exact running max of the raw scores
   }
-  bool redo = false;                          // a row outgrew its reference (see fold_max)
   const float cexp = p.c_log2;                 // softmax scale * log2(e) (* fp8 descales)
   // Keys visible from each of this lane's rows form one interval [vis_lo, vis_hi].
   int vis_lo[RB];
@@ -488,28 +483,35 @@ attn_fwd_kernel(const FwdParams p) {
     for (int r = 1; r < 16; ++r) m = fmaxf(m, x[r]);
     return m;
   };
-  // Fold a block's row maxima into the running state.  A row's reference max
-  // is fixed at the first block where it sees a key (O and l are still zero
-  // then, so nothing needs rescaling) and never moves afterwards: p may then
-  // exceed 1, up to 2^kGrowLimit, which the 16-bit P format and the fp32
-  // sums hold without overflow and with unchanged relative precision.  A row
-  // whose scores climb further sets `redo`; the workgroup then repeats the
-  // key loop with the exact row maximum (tracked in m_max) as reference.
-  auto fold_max = [&](const float (&mt)[RB]) {
+  // Reference max.  A row's reference is fixed at the first block where it
+  // sees a key (O and l are still zero then, so nothing needs rescaling) and
+  // never moves afterwards: later p may exceed 1, which the 16-bit P format
+  // and the fp32 sums hold with unchanged relative precision.  Only a p
+  // beyond the P format's range (2^16 in fp16, 2^128 in bf16) or an fp32
+  // overflow goes wrong, and it does so visibly: it leaves inf or NaN in l or
+  // O, which the epilogue checks; the workgroup then repeats the key loop with
+  // the exact row maximum as reference.  Block maxima are therefore computed
+  // only while some row of the wave has no reference yet (the first visible
+  // tile of each row).
+  auto wave_needs_ref = [&]() {
+    bool any = false;
+#pragma unroll
+    for (int qb = 0; qb < RB; ++qb) any = any || (m_run[qb] == -INFINITY);
+    return __builtin_amdgcn_ballot_w64(any) != 0;
+  };
+  auto fold_max = [&](const f32x16 (&s)[RB]) {
 #pragma unroll
     for (int qb = 0; qb < RB; ++qb) {
-      const float m = pair_max(mt[qb]);
-      m_max[qb] = fmaxf(m_max[qb], m);
       if (m_run[qb] == -INFINITY) {
+        const float m = pair_max(block_max(s[qb]));
         m_run[qb] = m;
         neg_mc[qb] = (m == -INFINITY) ? 0.f : -m * cexp;
-      } else {
-        redo = redo || ((m - m_run[qb]) * cexp > kGrowLimit);
       }
     }
   };
   // p = exp2(s c - m c) for a 32-key half of both row blocks, packed to 16
-  // bits; the row sum takes the unrounded fp32 p.
+  // bits; the row sum takes the unrounded fp32 p (the LSE needs it to fp32
+  // accuracy, which a sum of 16-bit p would miss by up to 2^-9).
   auto exp_pack = [&](const f32x16 (&s)[RB], uint32_t (&pk)[RB][8]) {
 #pragma unroll
     for (int qb = 0; qb < RB; ++qb)
@@ -563,12 +565,7 @@ attn_fwd_kernel(const FwdParams p) {
     uint32_t pa[RB][8], pb[RB][8];
     s_half(kl, 0, sa);
     if (masked) apply_mask(sa, k0, 0);
-    {
-      float mt[RB];
-#pragma unroll
-      for (int qb = 0; qb < RB; ++qb) mt[qb] = block_max(sa[qb]);
-      fold_max(mt);
-    }
+    if (wave_needs_ref()) fold_max(sa);
     __builtin_amdgcn_sched_barrier(0);
     s_half(kl, 1, sb);
     exp_pack(sa, pa);
@@ -585,12 +582,7 @@ attn_fwd_kernel(const FwdParams p) {
       residual(sa, pa, ra);              // same reference as pa: before the next fold
       pv_half<PIN, D, RB>(acc, ra, vl, lane, 0);
     }
-    {
-      float mt[RB];
-#pragma unroll
-      for (int qb = 0; qb < RB; ++qb) mt[qb] = block_max(sb[qb]);
-      fold_max(mt);
-    }
+    if (wave_needs_ref()) fold_max(sb);
     __builtin_amdgcn_sched_barrier(0);
     pv_half<PIN, D, RB>(acc, pa, vl, lane, 0);
     exp_pack(sb, pb);
@@ -614,46 +606,80 @@ attn_fwd_kernel(const FwdParams p) {
     if (block_none_visible(wr0, wr1, k0, k0 + kBN, n, p.causal, p.wl, p.wr)) return;
     compute_tile(kt, cur, !block_all_visible(wr0, wr1, k0, k0 + kBN, n, p.causal, p.wl, p.wr));
   };
+  // Exact row maxima (second pass only): S and the mask, no softmax.
+  float m_exact[RB];
+  auto max_step = [&](int kt, const unsigned char* cur) {
+    const int k0 = kt * kBN;
+    if (block_none_visible(wr0, wr1, k0, k0 + kBN, n, p.causal, p.wl, p.wr)) return;
+    const bool masked = !block_all_visible(wr0, wr1, k0, k0 + kBN, n, p.causal, p.wl, p.wr);
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      f32x16 s[RB];
+      s_half(cur, hb, s);
+      if (masked) apply_mask(s, k0, hb);
+#pragma unroll
+      for (int qb = 0; qb < RB; ++qb) m_exact[qb] = fmaxf(m_exact[qb], block_max(s[qb]));
+    }
+  };
 
-  // ---- main loop: tile kt is read from one stage while tile kt+1 lands in
-  // the other.  Each barrier publishes the next tile (its DMA must have
-  // landed, hence the full wait) and frees the stage just read.  A second
-  // pass runs only if some row outgrew its reference (see fold_max).
-  for (int pass = 0; pass < 2; ++pass) {
-    if (kt_begin < kt_end) {
-      issue_tile(kt_begin, stage0);
+  // ---- the key loop: tile kt is read from one stage while tile kt+1 lands
+  // in the other.  Each barrier publishes the next tile (its DMA must have
+  // landed, hence the full wait) and frees the stage just read.
+  auto walk = [&](auto&& step) {
+    if (kt_begin >= kt_end) return;
+    issue_tile(kt_begin, stage0);
+    store_v_fp8(stage0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    int kt = kt_begin;
+    while (true) {
+      issue_tile(min(kt + 1, kt_end - 1), stage1);
+      step(kt, stage0);
+      store_v_fp8(stage1);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (++kt == kt_end) break;
+      issue_tile(min(kt + 1, kt_end - 1), stage0);
+      step(kt, stage1);
       store_v_fp8(stage0);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      int kt = kt_begin;
-      while (true) {
-        issue_tile(min(kt + 1, kt_end - 1), stage1);
-        tile_step(kt, stage0);
-        store_v_fp8(stage1);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (++kt == kt_end) break;
-        issue_tile(min(kt + 1, kt_end - 1), stage0);
-        tile_step(kt, stage1);
-        store_v_fp8(stage0);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (++kt == kt_end) break;
-      }
+      if (++kt == kt_end) break;
     }
-    if (pass == 1 || !__syncthreads_or(redo ? 1 : 0)) break;
-    // restart every row of the workgroup from its exact maximum
+  };
+
+  // Pass 0 takes each row's reference from its first visible block.  If any
+  // row of the workgroup ended with inf or NaN in l or O (a p beyond the
+  // range of the P format, or an fp32 overflow), pass 1 recomputes the
+  // exact row maxima and repeats the key loop with them as references.
+  for (int pass = 0; pass < 2; ++pass) {
+    walk(tile_step);
+    if (pass == 1) break;
+    bool bad = false;
 #pragma unroll
     for (int qb = 0; qb < RB; ++qb) {
-      m_run[qb] = m_max[qb];
-      neg_mc[qb] = (m_max[qb] == -INFINITY) ? 0.f : -m_max[qb] * cexp;
+      float t = l_part[qb] + __shfl_xor(l_part[qb], 32);
+#pragma unroll
+      for (int c = 0; c < C::kDBlocks; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) t += acc[qb][c][r];
+      bad = bad || !__builtin_isfinite(t);
+    }
+    if (!__syncthreads_or(bad ? 1 : 0)) break;
+#pragma unroll
+    for (int qb = 0; qb < RB; ++qb) m_exact[qb] = -INFINITY;
+    walk(max_step);
+#pragma unroll
+    for (int qb = 0; qb < RB; ++qb) {
+      const float m = pair_max(m_exact[qb]);
+      m_run[qb] = m;
+      neg_mc[qb] = (m == -INFINITY) ? 0.f : -m * cexp;
       l_part[qb] = 0.f;
 #pragma unroll
       for (int c = 0; c < C::kDBlocks; ++c)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[qb][c][r] = 0.f;
     }
-    redo = false;
   }
 
   // ---- epilogue: O = O_acc / l (* v descale), LSE = ln(2) * (m c + log2 l)

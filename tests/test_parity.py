@@ -92,10 +92,13 @@ def test_workload_sampled(name):
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("causal", [False, True])
-def test_scores_outgrowing_the_first_tile(dtype, causal):
+@pytest.mark.parametrize("scale", [1.0, 2.0])
+def test_scores_outgrowing_the_first_tile(dtype, causal, scale):
     # Keys grow along the sequence, so late scores exceed the first tile's
-    # maximum by far more than the 16-bit P headroom: the kernel's second pass
-    # (exact row maximum as reference) must produce the right result.
+    # maximum by far: by about 2^86 (scale 1) or 2^172 (scale 2) in p.  The
+    # first exceeds fp16 P's range but not bf16's, the second overflows fp32
+    # exp2 too; either way the kernel must detect it and redo the row block
+    # with the exact row maximum as reference.
     import torch as _t
     from exact_attention_04_amd.workloads import Inputs, torch_dtype
     n, d = 700, 64
@@ -106,4 +109,4 @@ def test_scores_outgrowing_the_first_tile(dtype, causal):
     v = rng.standard_normal((1, n, 2, d)).astype(np.float32)
     td = torch_dtype(dtype)
     inp = Inputs(*(_t.from_numpy(x).to(td) for x in (q, k, v)), (1.0, 1.0, 1.0))
-    full_check(inp, dtype, causal=causal, scale=1.0, what=f"growing scores {dtype} causal={causal}")
+    full_check(inp, dtype, causal=causal, scale=scale, what=f"growing scores {dtype} causal={causal} scale={scale}")
