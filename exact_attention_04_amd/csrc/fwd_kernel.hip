@@ -189,26 +189,24 @@ __device__ __forceinline__ bool block_none_visible(int r0, int r1, int k0, int k
 // reads: within each 16-lane group, source lane sl points at key
 // base + sl/4, columns 4 (sl%4) .. +3, and lane i receives column i of the 4
 // consecutive keys.  Each fragment feeds both row blocks.
+//
+// `va[r8][c]` is this lane's byte offset, within a V tile, of its read for
+// key row 4 (g/2) + sl/4 + 8 r8 and column block c; moving by 16 or 32 key
+// rows leaves the swizzle unchanged, so every other read of the tile is that
+// offset plus a constant.
 template <In PIN, int D, int RB>
 __device__ __forceinline__ void pv_half(f32x16 (&acc)[RB][D / 32], const uint32_t (&pk)[RB][8],
-                                        const unsigned char* vl, int lane, int hb) {
-  const int g = lane >> 4;          // 16-lane group
-  const int sl = lane & 15;         // source lane within the group
+                                        const unsigned char* vl, const uint32_t (&va)[2][D / 32], int hb) {
   // the fragment reads of each 8-key step are issued together, ahead of its
   // MFMAs, so their latency is paid once per step rather than per MFMA
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
+    const unsigned char* base = vl + (32 * hb + 16 * j) * (2 * D);
     uint4 aop[D / 32];
-    const int vrow = 32 * hb + 16 * j + 4 * (g >> 1) + (sl >> 2);
 #pragma unroll
     for (int c = 0; c < D / 32; ++c) {
-      const int dcol = 32 * c + 16 * (g & 1) + 4 * (sl & 3);
-      const int unit = dcol >> 3;
-      const int hoff = (dcol & 7) * 2;
-      const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_i16x4*)(vl + lds_offset<2 * D>(vrow, unit) + hoff));
-      const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_i16x4*)(vl + lds_offset<2 * D>(vrow + 8, unit) + hoff));
+      const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + va[0][c]));
+      const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + va[1][c]));
       const uint2 w0 = __builtin_bit_cast(uint2, t0);
       const uint2 w1 = __builtin_bit_cast(uint2, t1);
       aop[c] = make_uint4(w0.x, w0.y, w1.x, w1.y);
@@ -345,15 +343,21 @@ attn_fwd_kernel(const FwdParams p) {
     return (row_bytes == 256 ? swizzled_unit<256>(row, phys) : swizzled_unit<128>(row, phys)) * 16;
   };
   // Byte offset, from the tile's first key, of the unit this lane fetches in
-  // DMA block `blk` (recomputed per tile: cheaper than keeping it live).
-  auto k_off = [&](int i) {
+  // each of its DMA blocks.  Computed once; the empty asm statements in
+  // issue_tile hide their origin from the compiler, so each load takes the
+  // tile base in SGPRs plus this 32-bit offset instead of a 64-bit address
+  // rebuilt per tile.
+  uint32_t k_off[kKBlocks], v_off[kVB];
+#pragma unroll
+  for (int i = 0; i < kKBlocks; ++i) {
     const int blk = wave * kKBlocks + i;
-    return (uint32_t)(dma_row(blk, C::kKRow) * k_row_stride + dma_col(blk, C::kKRow));
-  };
-  auto v_off = [&](int i) {
+    k_off[i] = (uint32_t)(dma_row(blk, C::kKRow) * k_row_stride + dma_col(blk, C::kKRow));
+  }
+#pragma unroll
+  for (int i = 0; i < kVB; ++i) {
     const int blk = wave * kVBlocks + i;
-    return (uint32_t)(dma_row(blk, C::kVRow) * v_row_stride + dma_col(blk, C::kVRow));
-  };
+    v_off[i] = kVBlocks > 0 ? (uint32_t)(dma_row(blk, C::kVRow) * v_row_stride + dma_col(blk, C::kVRow)) : 0u;
+  }
   uint4 vreg[C::kFp8 ? C::kVPer : 1];
   auto issue_tile = [&](int kt, unsigned char* dst) {
     const int k0 = kt * kBN;
@@ -362,14 +366,18 @@ attn_fwd_kernel(const FwdParams p) {
     const unsigned char* vb_ = vg + (int64_t)k0 * v_row_stride;
     if (last >= kBN - 1) {
 #pragma unroll
+      for (int i = 0; i < kKBlocks; ++i) asm volatile("" : "+v"(k_off[i]));
+#pragma unroll
+      for (int i = 0; i < kVBlocks; ++i) asm volatile("" : "+v"(v_off[i]));
+#pragma unroll
       for (int i = 0; i < kKBlocks; ++i)
-        __builtin_amdgcn_global_load_lds((const void*)(kb_ + k_off(i)),
+        __builtin_amdgcn_global_load_lds((const void*)(kb_ + k_off[i]),
                                          (__attribute__((address_space(3))) void*)(dst + (wave * kKBlocks + i) * 1024),
                                          16, 0, 0);
 #pragma unroll
       for (int i = 0; i < kVBlocks; ++i)
         __builtin_amdgcn_global_load_lds(
-            (const void*)(vb_ + v_off(i)),
+            (const void*)(vb_ + v_off[i]),
             (__attribute__((address_space(3))) void*)(dst + C::kKTile + (wave * kVBlocks + i) * 1024), 16, 0, 0);
     } else {
 #pragma unroll
@@ -438,6 +446,21 @@ attn_fwd_kernel(const FwdParams p) {
     if (p.causal) hi = min(hi, qi);
     if (p.wr >= 0) hi = min(hi, qi + p.wr);
     vis_span[qb] = (uint32_t)(hi - vis_lo[qb]);
+  }
+
+  // This lane's transposing-read offsets within a V tile (see pv_half).
+  uint32_t va[2][C::kDBlocks];
+  {
+    const int g = lane >> 4, sl = lane & 15;
+#pragma unroll
+    for (int r8 = 0; r8 < 2; ++r8)
+#pragma unroll
+      for (int c = 0; c < C::kDBlocks; ++c) {
+        const int vrow = 4 * (g >> 1) + (sl >> 2) + 8 * r8;
+        const int dcol = 32 * c + 16 * (g & 1) + 4 * (sl & 3);
+        va[r8][c] = (uint32_t)(lds_offset<C::kVRow>(vrow, dcol >> 3) + (dcol & 7) * 2);
+        asm volatile("" : "+v"(va[r8][c]));
+      }
   }
 
   // ---- building blocks over 32-key halves of a staged tile ----------------
@@ -580,11 +603,11 @@ attn_fwd_kernel(const FwdParams p) {
       apply_mask(sb, k0, 1);
       uint32_t ra[RB][8];
       residual(sa, pa, ra);              // same reference as pa: before the next fold
-      pv_half<PIN, D, RB>(acc, ra, vl, lane, 0);
+      pv_half<PIN, D, RB>(acc, ra, vl, va, 0);
     }
     if (wave_needs_ref()) fold_max(sb);
     __builtin_amdgcn_sched_barrier(0);
-    pv_half<PIN, D, RB>(acc, pa, vl, lane, 0);
+    pv_half<PIN, D, RB>(acc, pa, vl, va, 0);
     exp_pack(sb, pb);
 #pragma unroll
     for (int i = 0; i < kPVMfma; ++i) {
@@ -593,11 +616,11 @@ attn_fwd_kernel(const FwdParams p) {
       __builtin_amdgcn_sched_group_barrier(0x002, kExpValu / kPVMfma, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
-    pv_half<PIN, D, RB>(acc, pb, vl, lane, 1);
+    pv_half<PIN, D, RB>(acc, pb, vl, va, 1);
     if (masked) {
       uint32_t rb[RB][8];
       residual(sb, pb, rb);
-      pv_half<PIN, D, RB>(acc, rb, vl, lane, 1);
+      pv_half<PIN, D, RB>(acc, rb, vl, va, 1);
     }
   };
 
