@@ -50,6 +50,26 @@ def _run(cmd, verbose):
         print(out, flush=True)
 
 
+def elf_section_names(path: str) -> set:
+    """Section names of a 64-bit little-endian ELF file."""
+    import struct
+    with open(path, "rb") as f:
+        data = f.read()
+    if data[:4] != b"\x7fELF" or data[4] != 2 or data[5] != 1:
+        raise RuntimeError(f"{path}: not a 64-bit little-endian ELF file")
+    shoff, = struct.unpack_from("<Q", data, 0x28)
+    shentsize, shnum, shstrndx = struct.unpack_from("<HHH", data, 0x3A)
+    def sh(i):
+        return struct.unpack_from("<IIQQQQIIQQ", data, shoff + i * shentsize)
+    stroff = sh(shstrndx)[4]
+    names = set()
+    for i in range(shnum):
+        nm = sh(i)[0]
+        end = data.index(b"\0", stroff + nm)
+        names.add(data[stroff + nm:end].decode())
+    return names
+
+
 def build(verbose: bool = False, jobs: int = 4) -> str:
     """Compile the kernels and the ABI layer; returns the path of the library."""
     hipcc = _hipcc()
@@ -72,7 +92,11 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
             if out and verbose:
                 print(out, flush=True)
         tmp_lib = os.path.join(tmp, LIB_NAME)
-        _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp_lib] + objs, verbose)
+        # --no-undefined: a kernel whose host stub was not emitted must fail
+        # the build here, not the first call at run time
+        _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-Wl,--no-undefined", "-o", tmp_lib] + objs, verbose)
+        if ".hip_fatbin" not in elf_section_names(tmp_lib):
+            raise RuntimeError(f"{LIB_NAME} has no .hip_fatbin section: no GPU code was embedded")
         os.replace(tmp_lib, LIB_PATH)
     finally:
         shutil.rmtree(tmp, ignore_errors=True)

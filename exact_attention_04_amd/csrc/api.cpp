@@ -108,6 +108,8 @@ int validate(const ea_attn_args* a, bool* empty) {
   if (N >= lim / 2 || B * H >= lim) return EA_EUNSUPPORTED;
   for (int i = 0; i < 4; ++i) {
     if (strides[3 * i + 1] * N >= lim) return EA_EUNSUPPORTED;
+    // byte offsets within a 64-row K/V tile are 32-bit
+    if (strides[3 * i + 1] * 64 * 2 >= lim) return EA_EUNSUPPORTED;
   }
 
   const Span so = span_of(a->o, B, N, H, D, a->o_stride_b, a->o_stride_s, a->o_stride_h, eout);
@@ -118,30 +120,8 @@ int validate(const ea_attn_args* a, bool* empty) {
   return EA_OK;
 }
 
-// Tile configuration (see fwd_kernel.h).  The environment variable
-// EA_ATTN_TILE=bm128|bm256 overrides the choice (for tile sweeps); otherwise
-// the 128-row configuration is used.
-int choose_cfg(const ea_attn_args* /*a*/) {
-  static const int forced = [] {
-    const char* e = std::getenv("EA_ATTN_TILE");
-    if (e == nullptr) return -1;
-    if (std::strcmp(e, "bm128") == 0) return 0;
-    if (std::strcmp(e, "bm256") == 0) return 1;
-    return -1;
-  }();
-  if (forced >= 0) return forced;
-  return 0;
-}
-
-// Workgroup order (see the kernel).  EA_ATTN_SCHED=0|1 overrides it.
-int choose_sched() {
-  static const int forced = [] {
-    const char* e = std::getenv("EA_ATTN_SCHED");
-    if (e == nullptr) return -1;
-    return std::atoi(e) == 0 ? 0 : 1;
-  }();
-  return forced >= 0 ? forced : 0;
-}
+// Tile configuration (see fwd_kernel.h): a single one for now.
+int choose_cfg(const ea_attn_args* /*a*/) { return 0; }
 
 ea::FwdParams make_params(const ea_attn_args* a, int cfg) {
   ea::FwdParams p;
@@ -167,7 +147,6 @@ ea::FwdParams make_params(const ea_attn_args* a, int cfg) {
                    1.4426950408889634;
   p.c_log2 = (float)c;
   p.v_descale = fp8 ? a->v_descale : 1.0f;
-  p.sched = choose_sched();
   return p;
 }
 

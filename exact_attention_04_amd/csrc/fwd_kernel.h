@@ -19,13 +19,12 @@ struct FwdParams {
   int64_t o_sb, o_ss, o_sh;
   int64_t lse_sb, lse_sh;
   int causal, wl, wr;
-  int sched;             // workgroup order: 0 = heaviest tiles first, 1 = per-XCD head-major
   float c_log2;          // softmax_scale * q_descale * k_descale * log2(e)
   float v_descale;
 };
 
-// Tile configurations: 0 = 128 query rows per workgroup (32 per wave, two
-// waves per SIMD), 1 = 256 query rows (64 per wave, one wave per SIMD).
+// Tile configuration 0 (the only one): 128 query rows per workgroup (4 waves
+// of 32 rows, two waves per SIMD), 64 keys per K/V tile.
 int tile_bm(int cfg);
 int tile_waves(int cfg);
 int tile_bn();

@@ -142,6 +142,24 @@ __device__ __forceinline__ void fp8x16_to_bf16(uint4 in, uint4& lo, uint4& hi) {
   hi = make_uint4(o[4], o[5], o[6], o[7]);
 }
 
+// Buffer resource of `bytes` bytes at `base` (word 3 = 0x00020000: raw,
+// untyped access on this GPU family).  Offsets at or past `bytes` read as 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane L's bytes at
+// base + voff land at lds + 16 L (one instruction fills 1 KB).
+__device__ __forceinline__ void load_16b_to_lds(const void* base, int bytes, uint32_t voff, unsigned char* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(buffer_rsrc(base, bytes), (__attribute__((address_space(3))) void*)lds, 16,
+                                           voff, 0, 0, 0);
+}
+
+// 16 bytes from global memory into registers (0 past `bytes`).
+__device__ __forceinline__ uint4 load_16b(const void* base, int bytes, uint32_t voff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(buffer_rsrc(base, bytes), voff, 0, 0));
+}
+
 // Max over the two lanes l, l^32 of a wave (they hold the two key halves of
 // one query row).
 __device__ __forceinline__ float pair_max(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
@@ -222,6 +240,15 @@ __device__ __forceinline__ void pv_half(f32x16 (&acc)[RB][D / 32], const uint32_
   }
 }
 
+template <bool B>
+struct BoolTag {
+  static constexpr bool value = B;
+};
+template <int I>
+struct IntTag {
+  static constexpr int value = I;
+};
+
 template <In IN, int D, int WAVES, int RB>
 struct Cfg {
   static constexpr bool kFp8 = (IN == In::FP8);
@@ -247,14 +274,18 @@ attn_fwd_kernel(const FwdParams p) {
   using C = Cfg<IN, D, WAVES, RB>;
   constexpr In PIN = (IN == In::F16) ? In::F16 : In::BF16;   // type of P, V in LDS and O
   constexpr int kBM = C::kBM;
-  // Two stage buffers (K tile then V tile) at fixed offsets of one LDS array:
-  // the loop below is unrolled by two so that each half names its buffer at
-  // compile time (one address register serves both, with an immediate
-  // offset), and the LDS DMA into one buffer stays in flight while the other
-  // one is read.
-  __shared__ __attribute__((aligned(1024))) unsigned char stages[2 * C::kStage];
-  unsigned char* const stage0 = stages;
-  unsigned char* const stage1 = stages + C::kStage;
+  // LDS: two K slots and two V slots.  K of tile i+1 and V of tile i are
+  // read in the same iteration (the S MFMAs run one tile ahead of P.V), so
+  // the two rings are offset by one tile.  The loop is unrolled by two so that
+  // every slot is named at compile time (immediate offsets in the LDS
+  // instructions).  The slots are separate objects so that the compiler can
+  // tell the DMA into one slot from the reads of another: in a single array
+  // it cannot, and it then waits for the DMA just issued before the first
+  // read, which serialises the prefetch with the compute.
+  __shared__ __attribute__((aligned(1024))) unsigned char kbuf0[C::kKTile];
+  __shared__ __attribute__((aligned(1024))) unsigned char kbuf1[C::kKTile];
+  __shared__ __attribute__((aligned(1024))) unsigned char vbuf0[C::kVTile];
+  __shared__ __attribute__((aligned(1024))) unsigned char vbuf1[C::kVTile];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, kept in an SGPR
@@ -262,23 +293,12 @@ attn_fwd_kernel(const FwdParams p) {
   const int half = lane >> 5;      // which 16 of each 32 keys this lane holds
   const int col = lane & 31;       // the query row (within each row block) this lane owns
 
-  // ---- work assignment.  Workgroups are dealt to the 8 XCDs round-robin
-  // (workgroup i runs on XCD i % 8), each XCD with its own L2.  sched 1: XCD
-  // x serves heads x, x+8, x+16, ... one after another, all query tiles of a
-  // head back to back (heaviest first), so the tiles running together on an
-  // XCD read the same K/V through its L2.  sched 0 (or B*H not a multiple
-  // of 8): heaviest tiles of all heads first.
+  // ---- work assignment: heaviest query tiles first (causal tiles near the
+  // end of the sequence see the most keys), all heads of one tile index
+  // together.
   const int bh_count = p.batch * p.heads;
-  int tile, bh;
-  if (p.sched == 1 && bh_count % 8 == 0) {
-    const int xcd = (int)(blockIdx.x % 8u);
-    const int slot = (int)(blockIdx.x / 8u);
-    tile = p.q_tiles - 1 - slot % p.q_tiles;
-    bh = xcd + 8 * (slot / p.q_tiles);
-  } else {
-    tile = p.q_tiles - 1 - (int)(blockIdx.x / bh_count);
-    bh = (int)(blockIdx.x % bh_count);
-  }
+  const int tile = p.q_tiles - 1 - (int)(blockIdx.x / bh_count);
+  const int bh = (int)(blockIdx.x % bh_count);
   const int b = bh / p.heads;
   const int h = bh - b * p.heads;
   const int q0 = tile * kBM;
@@ -324,88 +344,83 @@ attn_fwd_kernel(const FwdParams p) {
     }
   }
 
-  // ---- staging of one K/V tile into LDS (swizzled layout).
+  // ---- staging of K and V tiles into LDS (swizzled layout).
   // 16-bit K and V, and fp8 K, go straight from global memory to LDS
-  // (global_load_lds_dwordx4): one wave instruction fills 1 KB of LDS, lane L
-  // writing 16-byte unit L of it, so each lane fetches the global unit that
-  // the swizzle maps to that LDS position.  In the last tile, keys past the
-  // end are clamped to the last key; those keys are masked (p = 0).
+  // (buffer_load_dwordx4 ... lds): one wave instruction fills 1 KB of LDS,
+  // lane L writing 16-byte unit L of it, so each lane fetches the global unit
+  // that the swizzle maps to that LDS position.  Each tile is addressed
+  // through a buffer resource whose range ends with the sequence's last key:
+  // rows past the end read as zeros (and are masked), so the last tile needs
+  // no special path, and a resource of range 0 turns a load into a no-op.
   // fp8 V goes through registers and is widened to bf16 on the way into LDS.
   constexpr int kKBlocks = C::kKTile / 1024 / WAVES;     // DMA instructions per wave, K
   constexpr int kVBlocks = C::kFp8 ? 0 : C::kVTile / 1024 / WAVES;
   constexpr int kVB = kVBlocks > 0 ? kVBlocks : 1;
-  // Tile row and byte column of the unit lane `lane` fetches in DMA block `blk`.
-  auto dma_row = [&](int blk, int row_bytes) { return (blk * 64 + lane) / (row_bytes / 16); };
-  auto dma_col = [&](int blk, int row_bytes) {
-    const int pos = blk * 64 + lane;
+  // Tile row and byte column of the unit lane `ln` fetches in DMA block `blk`.
+  auto dma_row = [](int blk, int row_bytes, int ln) { return (blk * 64 + ln) / (row_bytes / 16); };
+  auto dma_col = [](int blk, int row_bytes, int ln) {
+    const int pos = blk * 64 + ln;
     const int row = pos / (row_bytes / 16);
     const int phys = pos % (row_bytes / 16);
     return (row_bytes == 256 ? swizzled_unit<256>(row, phys) : swizzled_unit<128>(row, phys)) * 16;
   };
   // Byte offset, from the tile's first key, of the unit this lane fetches in
-  // each of its DMA blocks.  Computed once; the empty asm statements in
-  // issue_tile hide their origin from the compiler, so each load takes the
-  // tile base in SGPRs plus this 32-bit offset instead of a 64-bit address
-  // rebuilt per tile.
+  // each of its DMA blocks (< 2^31: the host bounds 64 rows of stride).
   uint32_t k_off[kKBlocks], v_off[kVB];
 #pragma unroll
   for (int i = 0; i < kKBlocks; ++i) {
     const int blk = wave * kKBlocks + i;
-    k_off[i] = (uint32_t)(dma_row(blk, C::kKRow) * k_row_stride + dma_col(blk, C::kKRow));
+    k_off[i] = (uint32_t)(dma_row(blk, C::kKRow, lane) * k_row_stride + dma_col(blk, C::kKRow, lane));
   }
 #pragma unroll
   for (int i = 0; i < kVB; ++i) {
     const int blk = wave * kVBlocks + i;
-    v_off[i] = kVBlocks > 0 ? (uint32_t)(dma_row(blk, C::kVRow) * v_row_stride + dma_col(blk, C::kVRow)) : 0u;
+    v_off[i] = kVBlocks > 0 ? (uint32_t)(dma_row(blk, C::kVRow, lane) * v_row_stride + dma_col(blk, C::kVRow, lane))
+                            : 0u;
   }
-  uint4 vreg[C::kFp8 ? C::kVPer : 1];
-  auto issue_tile = [&](int kt, unsigned char* dst) {
+  // Buffer range of tile kt of a K or V head: the tile's first key and the
+  // bytes up to the end of the sequence's last key (0 if kt >= kt_end).  The
+  // resource is built at each load from these plain values; the compiler
+  // shares the scalar work between the loads of a tile.
+  struct TileRange {
+    const unsigned char* base;
+    int bytes;
+  };
+  auto tile_range = [&](const unsigned char* head, int row_stride, int row_bytes, int kt) {
     const int k0 = kt * kBN;
-    const int last = n - 1 - k0;                               // last valid row of this tile
-    const unsigned char* kb_ = kg + (int64_t)k0 * k_row_stride;
-    const unsigned char* vb_ = vg + (int64_t)k0 * v_row_stride;
-    if (last >= kBN - 1) {
-#pragma unroll
-      for (int i = 0; i < kKBlocks; ++i) asm volatile("" : "+v"(k_off[i]));
-#pragma unroll
-      for (int i = 0; i < kVBlocks; ++i) asm volatile("" : "+v"(v_off[i]));
-#pragma unroll
-      for (int i = 0; i < kKBlocks; ++i)
-        __builtin_amdgcn_global_load_lds((const void*)(kb_ + k_off[i]),
-                                         (__attribute__((address_space(3))) void*)(dst + (wave * kKBlocks + i) * 1024),
-                                         16, 0, 0);
-#pragma unroll
-      for (int i = 0; i < kVBlocks; ++i)
-        __builtin_amdgcn_global_load_lds(
-            (const void*)(vb_ + v_off[i]),
-            (__attribute__((address_space(3))) void*)(dst + C::kKTile + (wave * kVBlocks + i) * 1024), 16, 0, 0);
-    } else {
-#pragma unroll
-      for (int i = 0; i < kKBlocks; ++i)
-        __builtin_amdgcn_global_load_lds(
-            (const void*)(kb_ + (uint32_t)(min(dma_row(wave * kKBlocks + i, C::kKRow), last) * k_row_stride +
-                                           dma_col(wave * kKBlocks + i, C::kKRow))),
-            (__attribute__((address_space(3))) void*)(dst + (wave * kKBlocks + i) * 1024), 16, 0, 0);
-#pragma unroll
-      for (int i = 0; i < kVBlocks; ++i)
-        __builtin_amdgcn_global_load_lds(
-            (const void*)(vb_ + (uint32_t)(min(dma_row(wave * kVBlocks + i, C::kVRow), last) * v_row_stride +
-                                           dma_col(wave * kVBlocks + i, C::kVRow))),
-            (__attribute__((address_space(3))) void*)(dst + C::kKTile + (wave * kVBlocks + i) * 1024), 16, 0, 0);
-    }
+    const int rows = kt < kt_end ? min(n - k0, kBN) : 0;
+    return TileRange{head + (int64_t)k0 * row_stride, rows > 0 ? (rows - 1) * row_stride + row_bytes : 0};
+  };
+  uint4 vreg[C::kFp8 ? C::kVPer : 1];
+  // One load of a tile: K block i, or V item i.
+  constexpr int kDmaK = kKBlocks;
+  constexpr int kDmaV = C::kFp8 ? C::kVPer : kVBlocks;
+  auto load_k = [&](TileRange t, unsigned char* dst, int i) {
+    load_16b_to_lds(t.base, t.bytes, k_off[i], dst + (wave * kKBlocks + i) * 1024);
+  };
+  auto load_v = [&](TileRange t, unsigned char* dst, int i) {
     if constexpr (C::kFp8) {
-#pragma unroll
-      for (int i = 0; i < C::kVPer; ++i) {
-        const int id = tid + i * C::kThreads;
-        const int r = min(id / (D / 16), last);
-        vreg[i] = *(const uint4*)(vb_ + (uint32_t)(r * v_row_stride + (id % (D / 16)) * 16));
-      }
+      const int id = tid + i * C::kThreads;
+      vreg[i] = load_16b(t.base, t.bytes, (uint32_t)((id / (D / 16)) * v_row_stride + (id % (D / 16)) * 16));
+    } else {
+      load_16b_to_lds(t.base, t.bytes, v_off[i], dst + (wave * kVBlocks + i) * 1024);
     }
   };
+  auto k_range = [&](int kt) { return tile_range(kg, k_row_stride, C::kKRow, kt); };
+  auto v_range = [&](int kt) { return tile_range(vg, v_row_stride, D * C::kInBytes, kt); };
+  auto issue_k = [&](int kt, unsigned char* dst) {
+    const TileRange t = k_range(kt);
+#pragma unroll
+    for (int i = 0; i < kDmaK; ++i) load_k(t, dst, i);
+  };
+  auto issue_v = [&](int kt, unsigned char* dst) {
+    const TileRange t = v_range(kt);
+#pragma unroll
+    for (int i = 0; i < kDmaV; ++i) load_v(t, dst, i);
+  };
   // fp8 only: widen the V tile held in registers and store it (bf16) to LDS.
-  auto store_v_fp8 = [&](unsigned char* dst) {
+  auto store_v_fp8 = [&](unsigned char* vl) {
     if constexpr (C::kFp8) {
-      unsigned char* vl = dst + C::kKTile;
 #pragma unroll
       for (int i = 0; i < C::kVPer; ++i) {
         const int id = tid + i * C::kThreads;
@@ -418,6 +433,12 @@ attn_fwd_kernel(const FwdParams p) {
       }
     }
   };
+  // V rows past the end of the sequence must hold finite values (they meet
+  // p = 0 in P.V): clear both V slots once.
+  for (int i = tid; i < C::kVTile / 16; i += C::kThreads) {
+    ((uint4*)vbuf0)[i] = make_uint4(0, 0, 0, 0);
+    ((uint4*)vbuf1)[i] = make_uint4(0, 0, 0, 0);
+  }
 
   // ---- running state, per row block
   f32x16 acc[RB][C::kDBlocks];
@@ -464,9 +485,9 @@ attn_fwd_kernel(const FwdParams p) {
   }
 
   // ---- building blocks over 32-key halves of a staged tile ----------------
-  // S^T for keys [32 hb, 32 hb + 32) of the tile whose K part is at `kl`, for
-  // both row blocks (each K fragment feeds two MFMAs).
-  auto s_half = [&](const unsigned char* kl, int hb, f32x16 (&s)[RB]) {
+  // S^T for keys [32 hb, 32 hb + 32) of the K tile at `kl`, for every row
+  // block (each K fragment feeds RB MFMAs).
+  auto s_half = [&](const unsigned char* kl, int hb, f32x16 (&s)[RB], auto&& hook) {
 #pragma unroll
     for (int qb = 0; qb < RB; ++qb)
 #pragma unroll
@@ -481,9 +502,11 @@ attn_fwd_kernel(const FwdParams p) {
         a[2 * st + 1] = *(const uint4*)(kl + lds_offset<C::kKRow>(krow, u0 + 1));
       }
 #pragma unroll
-      for (int st = 0; st < C::kQSteps; ++st)
+      for (int st = 0; st < C::kQSteps; ++st) {
 #pragma unroll
         for (int qb = 0; qb < RB; ++qb) s[qb] = mfma_fp8(a[2 * st], a[2 * st + 1], qf[qb][2 * st], qf[qb][2 * st + 1], s[qb]);
+        hook(st);
+      }
     } else {
       // K fragment reads are issued in groups ahead of their MFMAs, so their
       // latency is paid once per group rather than per MFMA
@@ -494,9 +517,11 @@ attn_fwd_kernel(const FwdParams p) {
 #pragma unroll
         for (int j = 0; j < kGroup; ++j) a[j] = *(const uint4*)(kl + lds_offset<C::kKRow>(krow, 2 * (st0 + j) + half));
 #pragma unroll
-        for (int j = 0; j < kGroup; ++j)
+        for (int j = 0; j < kGroup; ++j) {
 #pragma unroll
           for (int qb = 0; qb < RB; ++qb) s[qb] = mfma_16bit<IN>(a[j], qf[qb][st0 + j], s[qb]);
+          hook(st0 + j);
+        }
       }
     }
   };
@@ -522,17 +547,17 @@ attn_fwd_kernel(const FwdParams p) {
     for (int qb = 0; qb < RB; ++qb) any = any || (m_run[qb] == -INFINITY);
     return __builtin_amdgcn_ballot_w64(any) != 0;
   };
-  auto fold_max = [&](const f32x16 (&s)[RB]) {
+  auto fold_max = [&](const f32x16 (&sa)[RB], const f32x16 (&sb)[RB]) {
 #pragma unroll
     for (int qb = 0; qb < RB; ++qb) {
       if (m_run[qb] == -INFINITY) {
-        const float m = pair_max(block_max(s[qb]));
+        const float m = pair_max(fmaxf(block_max(sa[qb]), block_max(sb[qb])));
         m_run[qb] = m;
         neg_mc[qb] = (m == -INFINITY) ? 0.f : -m * cexp;
       }
     }
   };
-  // p = exp2(s c - m c) for a 32-key half of both row blocks, packed to 16
+  // p = exp2(s c - m c) for a 32-key half of every row block, packed to 16
   // bits; the row sum takes the unrounded fp32 p (the LSE needs it to fp32
   // accuracy, which a sum of 16-bit p would miss by up to 2^-9).
   auto exp_pack = [&](const f32x16 (&s)[RB], uint32_t (&pk)[RB][8]) {
@@ -571,103 +596,150 @@ attn_fwd_kernel(const FwdParams p) {
       }
     }
   };
+  // Tiles crossing a mask edge or the sequence end, for this wave's rows.
+  auto tile_masked = [&](int kt) {
+    const int k0 = kt * kBN;
+    return !block_all_visible(wr0, wr1, k0, k0 + kBN, n, p.causal, p.wl, p.wr);
+  };
 
-  // ---- one tile: software-pipelined halves a (keys 0-31), b (32-63).
-  // `masked` (wave-uniform): the tile crosses a mask edge or the sequence
-  // end.  Its scores are masked, and the 16-bit rounding residual of p goes
-  // through a second P.V pass -- these tiles hold the rows with few visible
-  // keys, where the rounding of p does not average out.
+  // ---- one 32-key half ("unit") of the software pipeline.  The softmax of
+  // the current scores `sc` (tile kt, half hb) runs interleaved with the S
+  // MFMAs of the same half of the next tile (`sn`, from the K slot `kn`),
+  // then O += P V over the current V slot `vl`.  Issue is in order per wave,
+  // so this interleave is what lets the vector ALU and the matrix core work
+  // at the same time.  `masked`: tile kt crosses a mask edge or the sequence
+  // end; its rows include those with few visible keys, where the 16-bit
+  // rounding of p does not average out, so the rounding residual goes through
+  // a second P.V pass.
   constexpr int kSMfma = RB * C::kQSteps;            // S MFMAs per half (all row blocks)
-  constexpr int kPVMfma = RB * 2 * C::kDBlocks;      // P.V MFMAs per half
   constexpr int kExpValu = RB * 56;                  // softmax VALU per half (all row blocks)
-  auto compute_tile = [&](int kt, const unsigned char* cur, bool masked) {
-    const int k0 = kt * kBN;
-    const unsigned char* kl = cur;
-    const unsigned char* vl = cur + C::kKTile;
-    f32x16 sa[RB], sb[RB];
-    uint32_t pa[RB][8], pb[RB][8];
-    s_half(kl, 0, sa);
-    if (masked) apply_mask(sa, k0, 0);
-    if (wave_needs_ref()) fold_max(sa);
-    __builtin_amdgcn_sched_barrier(0);
-    s_half(kl, 1, sb);
-    exp_pack(sa, pa);
+  // `hook(st)` runs after the S MFMA of k-step st; the first unit of an
+  // iteration uses it to issue the loads of later tiles a few at a time, so
+  // they are spread between the MFMAs rather than issued in one burst, which
+  // would stall the waves that leave a barrier together on the address unit.
+  // (The scheduler cannot move those loads past LDS reads by itself: they
+  // write LDS.)
+  auto unit = [&](auto next_tag, auto dma_tag, f32x16 (&sc)[RB], bool masked, int hb, const unsigned char* vl,
+                  const unsigned char* kn, f32x16 (&sn)[RB], auto&& hook) {
+    uint32_t pk[RB][8];
+    if constexpr (decltype(next_tag)::value) {
+      // raised priority while the S MFMAs and the softmax interleave: when
+      // both waves of a SIMD have work, the one feeding the matrix core from
+      // this phase issues first
+      __builtin_amdgcn_s_setprio(1);
+      s_half(kn, hb, sn, hook);
+      exp_pack(sc, pk);
 #pragma unroll
-    for (int i = 0; i < kSMfma; ++i) {
-      if (i % (4 * RB) == 0) __builtin_amdgcn_sched_group_barrier(0x100, C::kFp8 ? 2 * C::kQSteps : 4, 0);  // K reads
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                  // S_b MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, kExpValu / kSMfma, 0);                  // softmax VALU
+      for (int i = 0; i < kSMfma; ++i) {
+        if (i % (4 * RB) == 0) __builtin_amdgcn_sched_group_barrier(0x100, C::kFp8 ? 2 * C::kQSteps : 4, 0);  // K reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                  // S MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, kExpValu / kSMfma, 0);                  // softmax VALU
+        if constexpr (decltype(dma_tag)::value > 0)
+          __builtin_amdgcn_sched_group_barrier(0x010, (decltype(dma_tag)::value + kSMfma - 1) / kSMfma, 0);  // loads
+      }
+    } else {
+      exp_pack(sc, pk);
     }
     __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
     if (masked) {
-      apply_mask(sb, k0, 1);
-      uint32_t ra[RB][8];
-      residual(sa, pa, ra);              // same reference as pa: before the next fold
-      pv_half<PIN, D, RB>(acc, ra, vl, va, 0);
+      uint32_t pr[RB][8];
+      residual(sc, pk, pr);
+      pv_half<PIN, D, RB>(acc, pr, vl, va, hb);
     }
-    if (wave_needs_ref()) fold_max(sb);
+    pv_half<PIN, D, RB>(acc, pk, vl, va, hb);
     __builtin_amdgcn_sched_barrier(0);
-    pv_half<PIN, D, RB>(acc, pa, vl, va, 0);
-    exp_pack(sb, pb);
-#pragma unroll
-    for (int i = 0; i < kPVMfma; ++i) {
-      if (i % (RB * C::kDBlocks) == 0) __builtin_amdgcn_sched_group_barrier(0x100, 2 * C::kDBlocks, 0);  // V^T reads
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                  // P_a.V MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, kExpValu / kPVMfma, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    pv_half<PIN, D, RB>(acc, pb, vl, va, 1);
-    if (masked) {
-      uint32_t rb[RB][8];
-      residual(sb, pb, rb);
-      pv_half<PIN, D, RB>(acc, rb, vl, va, 1);
-    }
   };
 
-  auto tile_step = [&](int kt, const unsigned char* cur) {
-    const int k0 = kt * kBN;
-    if (block_none_visible(wr0, wr1, k0, k0 + kBN, n, p.causal, p.wl, p.wr)) return;
-    compute_tile(kt, cur, !block_all_visible(wr0, wr1, k0, k0 + kBN, n, p.causal, p.wl, p.wr));
-  };
-  // Exact row maxima (second pass only): S and the mask, no softmax.
-  float m_exact[RB];
-  auto max_step = [&](int kt, const unsigned char* cur) {
-    const int k0 = kt * kBN;
-    if (block_none_visible(wr0, wr1, k0, k0 + kBN, n, p.causal, p.wl, p.wr)) return;
-    const bool masked = !block_all_visible(wr0, wr1, k0, k0 + kBN, n, p.causal, p.wl, p.wr);
+  // ---- the key loop.  Iteration i (tile kt = kt_begin + i) starts with the
+  // scores S(i) in registers, K(i+1) and V(i) in LDS; it issues the DMA of
+  // K(i+2) and V(i+1) into the slots freed by the previous iteration, runs
+  // the two units, and ends with a barrier once its DMA has landed.
+  f32x16 s_a[RB], s_b[RB];
+  auto iter = [&](int kt, const unsigned char* kread, const unsigned char* vread, unsigned char* kwrite,
+                  unsigned char* vwrite, bool& m_cur) {
+    if (wave_needs_ref()) fold_max(s_a, s_b);
+    const bool m_next = tile_masked(kt + 1);
+    f32x16 n_a[RB], n_b[RB];
+    // K(kt+2) (a no-op past the last tile) and V(kt+1), into the slots the
+    // previous iteration freed, spread over the S MFMAs of the first unit
+    const TileRange rk = k_range(kt + 2), rv = v_range(kt + 1);
+    constexpr int kPer = (kDmaK + kDmaV + C::kQSteps - 1) / C::kQSteps;
+    unit(BoolTag<true>{}, IntTag<kDmaK + kDmaV>{}, s_a, m_cur, 0, vread, kread, n_a, [&](int st) {
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      f32x16 s[RB];
-      s_half(cur, hb, s);
-      if (masked) apply_mask(s, k0, hb);
+      for (int u = 0; u < kPer; ++u) {
+        const int i = st * kPer + u;
+        if (i < kDmaK) load_k(rk, kwrite, i);
+        else if (i < kDmaK + kDmaV) load_v(rv, vwrite, i - kDmaK);
+      }
+    });
+    if (m_next) apply_mask(n_a, (kt + 1) * kBN, 0);
+    unit(BoolTag<true>{}, IntTag<0>{}, s_b, m_cur, 1, vread, kread, n_b, [](int) {});
+    if (m_next) apply_mask(n_b, (kt + 1) * kBN, 1);
 #pragma unroll
-      for (int qb = 0; qb < RB; ++qb) m_exact[qb] = fmaxf(m_exact[qb], block_max(s[qb]));
+    for (int qb = 0; qb < RB; ++qb) {
+      s_a[qb] = n_a[qb];
+      s_b[qb] = n_b[qb];
     }
-  };
-
-  // ---- the key loop: tile kt is read from one stage while tile kt+1 lands
-  // in the other.  Each barrier publishes the next tile (its DMA must have
-  // landed, hence the full wait) and frees the stage just read.
-  auto walk = [&](auto&& step) {
-    if (kt_begin >= kt_end) return;
-    issue_tile(kt_begin, stage0);
-    store_v_fp8(stage0);
+    m_cur = m_next;
+    store_v_fp8(vwrite);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+  };
+  auto key_loop = [&]() {
+    if (kt_begin >= kt_end) return;
+    issue_k(kt_begin, kbuf0);
+    issue_v(kt_begin, vbuf0);
+    store_v_fp8(vbuf0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    issue_k(kt_begin + 1, kbuf1);   // a no-op if there is no second tile
+    s_half(kbuf0, 0, s_a, [](int) {});
+    s_half(kbuf0, 1, s_b, [](int) {});
+    bool m_cur = tile_masked(kt_begin);
+    if (m_cur) {
+      apply_mask(s_a, kt_begin * kBN, 0);
+      apply_mask(s_b, kt_begin * kBN, 1);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    // tiles with a successor: pairs (static slot names), then an odd one
+    const int with_next = kt_end - 1 - kt_begin;
     int kt = kt_begin;
-    while (true) {
-      issue_tile(min(kt + 1, kt_end - 1), stage1);
-      step(kt, stage0);
-      store_v_fp8(stage1);
+    for (int j = 0; j < with_next / 2; ++j, kt += 2) {
+      iter(kt, kbuf1, vbuf0, kbuf0, vbuf1, m_cur);
+      iter(kt + 1, kbuf0, vbuf1, kbuf1, vbuf0, m_cur);
+    }
+    const bool odd = (with_next & 1) != 0;
+    if (odd) {
+      iter(kt, kbuf1, vbuf0, kbuf0, vbuf1, m_cur);
+      ++kt;
+    }
+    // last tile: softmax and P.V only
+    const unsigned char* vlast = odd ? vbuf1 : vbuf0;
+    if (wave_needs_ref()) fold_max(s_a, s_b);
+    unit(BoolTag<false>{}, IntTag<0>{}, s_a, m_cur, 0, vlast, kbuf0, s_a, [](int) {});
+    unit(BoolTag<false>{}, IntTag<0>{}, s_b, m_cur, 1, vlast, kbuf0, s_b, [](int) {});
+    __syncthreads();   // the slots are reused by a second pass
+  };
+  // Exact row maxima (second pass only): S and the mask, no softmax; one K
+  // tile at a time, no prefetch.
+  float m_exact[RB];
+  auto max_loop = [&]() {
+    for (int kt = kt_begin; kt < kt_end; ++kt) {
+      issue_k(kt, kbuf0);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      if (++kt == kt_end) break;
-      issue_tile(min(kt + 1, kt_end - 1), stage0);
-      step(kt, stage1);
-      store_v_fp8(stage0);
-      __builtin_amdgcn_s_waitcnt(0);
+      const bool masked = tile_masked(kt);
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        f32x16 s[RB];
+        s_half(kbuf0, hb, s, [](int) {});
+        if (masked) apply_mask(s, kt * kBN, hb);
+#pragma unroll
+        for (int qb = 0; qb < RB; ++qb) m_exact[qb] = fmaxf(m_exact[qb], block_max(s[qb]));
+      }
       __syncthreads();
-      if (++kt == kt_end) break;
     }
   };
 
@@ -676,7 +748,7 @@ attn_fwd_kernel(const FwdParams p) {
   // range of the P format, or an fp32 overflow), pass 1 recomputes the
   // exact row maxima and repeats the key loop with them as references.
   for (int pass = 0; pass < 2; ++pass) {
-    walk(tile_step);
+    key_loop();
     if (pass == 1) break;
     bool bad = false;
 #pragma unroll
@@ -691,7 +763,7 @@ attn_fwd_kernel(const FwdParams p) {
     if (!__syncthreads_or(bad ? 1 : 0)) break;
 #pragma unroll
     for (int qb = 0; qb < RB; ++qb) m_exact[qb] = -INFINITY;
-    walk(max_step);
+    max_loop();
 #pragma unroll
     for (int qb = 0; qb < RB; ++qb) {
       const float m = pair_max(m_exact[qb]);
@@ -745,9 +817,9 @@ static hipError_t launch_t(const FwdParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Tile configurations: 0 = 128 query rows (4 waves x 32 rows, two waves per
-// SIMD), 1 = 256 query rows (4 waves x 64 rows, one wave per SIMD).
-int tile_bm(int cfg) { return cfg == 1 ? 256 : 128; }
+// One tile configuration: 128 query rows per workgroup (4 waves x 32 rows,
+// two workgroups per CU), 64 keys per K/V tile.
+int tile_bm(int /*cfg*/) { return 128; }
 int tile_waves(int /*cfg*/) { return 4; }
 int tile_bn() { return kBN; }
 
@@ -757,33 +829,23 @@ int lds_bytes(int in_dtype, int d) {
   return 2 * (kBN * d * kin + kBN * d * 2);
 }
 
-template <int RB>
-static hipError_t launch_cfg(const FwdParams& p, int in_dtype, int d, hipStream_t stream) {
-  if (in_dtype == 1 && d == 64) return launch_t<In::F16, 64, 4, RB>(p, stream);
-  if (in_dtype == 1 && d == 128) return launch_t<In::F16, 128, 4, RB>(p, stream);
-  if (in_dtype == 2 && d == 64) return launch_t<In::BF16, 64, 4, RB>(p, stream);
-  if (in_dtype == 2 && d == 128) return launch_t<In::BF16, 128, 4, RB>(p, stream);
-  if (in_dtype == 3 && d == 128) return launch_t<In::FP8, 128, 4, RB>(p, stream);
-  return hipErrorInvalidValue;
-}
-
 hipError_t launch_fwd(const FwdParams& p, int in_dtype, int d, int cfg, hipStream_t stream) {
   // in_dtype: 1 = f16, 2 = bf16, 3 = fp8 e4m3 (validated by the caller)
-  if (cfg == 0) return launch_cfg<1>(p, in_dtype, d, stream);
-  if (cfg == 1) return launch_cfg<2>(p, in_dtype, d, stream);
+  if (cfg != 0) return hipErrorInvalidValue;
+  if (in_dtype == 1 && d == 64) return launch_t<In::F16, 64, 4, 1>(p, stream);
+  if (in_dtype == 1 && d == 128) return launch_t<In::F16, 128, 4, 1>(p, stream);
+  if (in_dtype == 2 && d == 64) return launch_t<In::BF16, 64, 4, 1>(p, stream);
+  if (in_dtype == 2 && d == 128) return launch_t<In::BF16, 128, 4, 1>(p, stream);
+  if (in_dtype == 3 && d == 128) return launch_t<In::FP8, 128, 4, 1>(p, stream);
   return hipErrorInvalidValue;
 }
 
-const char* kernel_name(int in_dtype, int d, int cfg) {
-  static const char* names[2][3][2] = {
-      {{"attn_fwd<f16,d64,bm128,bn64>", "attn_fwd<f16,d128,bm128,bn64>"},
-       {"attn_fwd<bf16,d64,bm128,bn64>", "attn_fwd<bf16,d128,bm128,bn64>"},
-       {"none", "attn_fwd<fp8,d128,bm128,bn64>"}},
-      {{"attn_fwd<f16,d64,bm256,bn64>", "attn_fwd<f16,d128,bm256,bn64>"},
-       {"attn_fwd<bf16,d64,bm256,bn64>", "attn_fwd<bf16,d128,bm256,bn64>"},
-       {"none", "attn_fwd<fp8,d128,bm256,bn64>"}}};
-  if (in_dtype < 1 || in_dtype > 3 || (d != 64 && d != 128) || (cfg != 0 && cfg != 1)) return "none";
-  return names[cfg][in_dtype - 1][d == 128];
+const char* kernel_name(int in_dtype, int d, int /*cfg*/) {
+  static const char* names[3][2] = {{"attn_fwd<f16,d64,bm128,bn64>", "attn_fwd<f16,d128,bm128,bn64>"},
+                                    {"attn_fwd<bf16,d64,bm128,bn64>", "attn_fwd<bf16,d128,bm128,bn64>"},
+                                    {"none", "attn_fwd<fp8,d128,bm128,bn64>"}};
+  if (in_dtype < 1 || in_dtype > 3 || (d != 64 && d != 128)) return "none";
+  return names[in_dtype - 1][d == 128];
 }
 
 }  // namespace ea

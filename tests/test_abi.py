@@ -39,6 +39,11 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(_lib.lib(), name)
 
 
+def test_library_embeds_gpu_code():
+    from exact_attention_04_amd.build import elf_section_names
+    assert ".hip_fatbin" in elf_section_names(_lib.LIB_PATH)
+
+
 def test_abi_version_and_status_strings():
     assert _lib.lib().ea_abi_version() == _lib.EA_ABI_VERSION
     for code in range(5):
