@@ -484,6 +484,15 @@ attn_fwd_kernel(const FwdParams p) {
       }
   }
 
+  // This lane's K-fragment read offsets within a K tile, for k-step st of the
+  // first 32 keys (the second 32 keys add a constant).
+  uint32_t ka[C::kQSteps];
+#pragma unroll
+  for (int st = 0; st < C::kQSteps; ++st) {
+    ka[st] = C::kFp8 ? 0u : (uint32_t)lds_offset<C::kKRow>(col, 2 * st + half);
+    asm volatile("" : "+v"(ka[st]));
+  }
+
   // ---- building blocks over 32-key halves of a staged tile ----------------
   // S^T for keys [32 hb, 32 hb + 32) of the K tile at `kl`, for every row
   // block (each K fragment feeds RB MFMAs).
@@ -584,6 +593,46 @@ attn_fwd_kernel(const FwdParams p) {
         pr[qb][r] = pack2<PIN>(e0 - unpack_lo<PIN>(pk[qb][r]), e1 - unpack_hi<PIN>(pk[qb][r]));
       }
   };
+  // S MFMAs of one half (K tile at `kn`) interleaved, step by step in program
+  // order, with the softmax of the current half `sc`: step st issues the
+  // MFMA of k-step st, the read of a K fragment kPre steps ahead, the
+  // loads `hook(st)` and the exp / sum / pack of 1 / kQSteps of the scores.
+  // Each step is fenced (sched_barrier), so the compiler keeps this order
+  // instead of grouping the MFMAs and the vector work apart (16-bit inputs).
+  auto s_phase = [&](const unsigned char* kn, int hb, f32x16 (&sn)[RB], const f32x16 (&sc)[RB],
+                     uint32_t (&pk)[RB][8], auto&& hook) {
+    constexpr int kSteps = C::kQSteps;
+    constexpr int kPre = kSteps < 4 ? kSteps : 4;      // K reads in flight
+    constexpr int kPairsPerStep = 8 / kSteps;          // packed P pairs per step
+#pragma unroll
+    for (int qb = 0; qb < RB; ++qb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sn[qb][r] = 0.f;
+    const unsigned char* kb = kn + 32 * hb * C::kKRow;
+    uint4 a[kSteps];
+#pragma unroll
+    for (int st = 0; st < kPre; ++st) a[st] = *(const uint4*)(kb + ka[st]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int st = 0; st < kSteps; ++st) {
+      if (st + kPre < kSteps) a[st + kPre] = *(const uint4*)(kb + ka[st + kPre]);
+#pragma unroll
+      for (int qb = 0; qb < RB; ++qb) sn[qb] = mfma_16bit<IN>(a[st], qf[qb][st], sn[qb]);
+      hook(st);
+#pragma unroll
+      for (int qb = 0; qb < RB; ++qb)
+#pragma unroll
+        for (int u = 0; u < kPairsPerStep; ++u) {
+          const int r = st * kPairsPerStep + u;
+          const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[qb][2 * r], cexp, neg_mc[qb]));
+          const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[qb][2 * r + 1], cexp, neg_mc[qb]));
+          l_part[qb] += e0;
+          l_part[qb] += e1;
+          pk[qb][r] = pack2<PIN>(e0, e1);
+        }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
   // Mask a 32-key half: key k0 + 32 hb + 8 (r/4) + 4 half + (r%4).
   auto apply_mask = [&](f32x16 (&s)[RB], int k0, int hb) {
 #pragma unroll
@@ -627,15 +676,17 @@ attn_fwd_kernel(const FwdParams p) {
       // both waves of a SIMD have work, the one feeding the matrix core from
       // this phase issues first
       __builtin_amdgcn_s_setprio(1);
-      s_half(kn, hb, sn, hook);
-      exp_pack(sc, pk);
+      if constexpr (C::kFp8) {
+        s_half(kn, hb, sn, hook);
+        exp_pack(sc, pk);
 #pragma unroll
-      for (int i = 0; i < kSMfma; ++i) {
-        if (i % (4 * RB) == 0) __builtin_amdgcn_sched_group_barrier(0x100, C::kFp8 ? 2 * C::kQSteps : 4, 0);  // K reads
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                  // S MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, kExpValu / kSMfma, 0);                  // softmax VALU
-        if constexpr (decltype(dma_tag)::value > 0)
-          __builtin_amdgcn_sched_group_barrier(0x010, (decltype(dma_tag)::value + kSMfma - 1) / kSMfma, 0);  // loads
+        for (int i = 0; i < kSMfma; ++i) {
+          if (i % (4 * RB) == 0) __builtin_amdgcn_sched_group_barrier(0x100, 2 * C::kQSteps, 0);  // K reads
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                  // S MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, kExpValu / kSMfma, 0);                  // softmax VALU
+        }
+      } else {
+        s_phase(kn, hb, sn, sc, pk, hook);
       }
     } else {
       exp_pack(sc, pk);
