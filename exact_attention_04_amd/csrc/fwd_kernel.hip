@@ -434,11 +434,13 @@ attn_fwd_kernel(const FwdParams p) {
     }
   };
   // V rows past the end of the sequence must hold finite values (they meet
-  // p = 0 in P.V): clear both V slots once.
+  // p = 0 in P.V): clear both V slots once.  The barrier orders these stores
+  // before any wave's first V load into the slots.
   for (int i = tid; i < C::kVTile / 16; i += C::kThreads) {
     ((uint4*)vbuf0)[i] = make_uint4(0, 0, 0, 0);
     ((uint4*)vbuf1)[i] = make_uint4(0, 0, 0, 0);
   }
+  __syncthreads();
 
   // ---- running state, per row block
   f32x16 acc[RB][C::kDBlocks];
@@ -657,9 +659,13 @@ attn_fwd_kernel(const FwdParams p) {
   // then O += P V over the current V slot `vl`.  Issue is in order per wave,
   // so this interleave is what lets the vector ALU and the matrix core work
   // at the same time.  `masked`: tile kt crosses a mask edge or the sequence
-  // end; its rows include those with few visible keys, where the 16-bit
-  // rounding of p does not average out, so the rounding residual goes through
-  // a second P.V pass.
+  // end.  On such tiles the 16-bit rounding of p can matter: when the half
+  // carries a large share of a row's weight (the first keys of a row, or a
+  // row whose weight concentrates on its latest keys), its rounding errors do
+  // not average out against the rest of the row.  If for some row of the
+  // wave the half adds more than 1/16 of the row's sum so far, the rounding
+  // residual p - round16(p) goes through a second P.V pass; otherwise its
+  // contribution to the error is below 2^-13 of max |v|.
   constexpr int kSMfma = RB * C::kQSteps;            // S MFMAs per half (all row blocks)
   constexpr int kExpValu = RB * 56;                  // softmax VALU per half (all row blocks)
   // `hook(st)` runs after the S MFMA of k-step st; the first unit of an
@@ -671,6 +677,9 @@ attn_fwd_kernel(const FwdParams p) {
   auto unit = [&](auto next_tag, auto dma_tag, f32x16 (&sc)[RB], bool masked, int hb, const unsigned char* vl,
                   const unsigned char* kn, f32x16 (&sn)[RB], auto&& hook) {
     uint32_t pk[RB][8];
+    float l_before[RB];
+#pragma unroll
+    for (int qb = 0; qb < RB; ++qb) l_before[qb] = l_part[qb];
     if constexpr (decltype(next_tag)::value) {
       // raised priority while the S MFMAs and the softmax interleave: when
       // both waves of a SIMD have work, the one feeding the matrix core from
@@ -693,7 +702,10 @@ attn_fwd_kernel(const FwdParams p) {
     }
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(0);
-    if (masked) {
+    bool heavy = false;
+#pragma unroll
+    for (int qb = 0; qb < RB; ++qb) heavy = heavy || ((l_part[qb] - l_before[qb]) * 16.f > l_part[qb]);
+    if (masked && __builtin_amdgcn_ballot_w64(heavy) != 0) {
       uint32_t pr[RB][8];
       residual(sc, pk, pr);
       pv_half<PIN, D, RB>(acc, pr, vl, va, hb);
