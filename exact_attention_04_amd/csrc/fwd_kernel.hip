@@ -350,8 +350,10 @@ attn_fwd_kernel(const FwdParams p) {
   // lane L writing 16-byte unit L of it, so each lane fetches the global unit
   // that the swizzle maps to that LDS position.  Each tile is addressed
   // through a buffer resource whose range ends with the sequence's last key:
-  // rows past the end read as zeros (and are masked), so the last tile needs
-  // no special path, and a resource of range 0 turns a load into a no-op.
+  // rows past the end are written as zeros (K: masked; V: met by p = 0), so
+  // the last tile needs no special path and the slots need no clearing.  A
+  // resource of range 0 (a tile past the visible range) makes the load write
+  // zeros, into a slot that is then never read.
   // fp8 V goes through registers and is widened to bf16 on the way into LDS.
   constexpr int kKBlocks = C::kKTile / 1024 / WAVES;     // DMA instructions per wave, K
   constexpr int kVBlocks = C::kFp8 ? 0 : C::kVTile / 1024 / WAVES;
@@ -433,15 +435,6 @@ attn_fwd_kernel(const FwdParams p) {
       }
     }
   };
-  // V rows past the end of the sequence must hold finite values (they meet
-  // p = 0 in P.V): clear both V slots once.  The barrier orders these stores
-  // before any wave's first V load into the slots.
-  for (int i = tid; i < C::kVTile / 16; i += C::kThreads) {
-    ((uint4*)vbuf0)[i] = make_uint4(0, 0, 0, 0);
-    ((uint4*)vbuf1)[i] = make_uint4(0, 0, 0, 0);
-  }
-  __syncthreads();
-
   // ---- running state, per row block
   f32x16 acc[RB][C::kDBlocks];
 #pragma unroll
@@ -724,7 +717,7 @@ attn_fwd_kernel(const FwdParams p) {
     if (wave_needs_ref()) fold_max(s_a, s_b);
     const bool m_next = tile_masked(kt + 1);
     f32x16 n_a[RB], n_b[RB];
-    // K(kt+2) (a no-op past the last tile) and V(kt+1), into the slots the
+    // K(kt+2) (zeros past the last tile) and V(kt+1), into the slots the
     // previous iteration freed, spread over the S MFMAs of the first unit
     const TileRange rk = k_range(kt + 2), rv = v_range(kt + 1);
     constexpr int kPer = (kDmaK + kDmaV + C::kQSteps - 1) / C::kQSteps;
@@ -753,10 +746,10 @@ attn_fwd_kernel(const FwdParams p) {
     if (kt_begin >= kt_end) return;
     issue_k(kt_begin, kbuf0);
     issue_v(kt_begin, vbuf0);
+    issue_k(kt_begin + 1, kbuf1);   // zeros if there is no second tile
     store_v_fp8(vbuf0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    issue_k(kt_begin + 1, kbuf1);   // a no-op if there is no second tile
     s_half(kbuf0, 0, s_a, [](int) {});
     s_half(kbuf0, 1, s_b, [](int) {});
     bool m_cur = tile_masked(kt_begin);
@@ -764,8 +757,7 @@ attn_fwd_kernel(const FwdParams p) {
       apply_mask(s_a, kt_begin * kBN, 0);
       apply_mask(s_b, kt_begin * kBN, 1);
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    __syncthreads();   // every wave is done with K(kt_begin) before its slot is refilled
     // tiles with a successor: pairs (static slot names), then an odd one
     const int with_next = kt_end - 1 - kt_begin;
     int kt = kt_begin;
