@@ -14,5 +14,6 @@ from .sdpa_fp64 import (  # noqa: F401
     attention_probs_head,
     attention_parallel,
     dequantize_e4m3,
+    kv_head_of,
     visible,
 )

@@ -26,12 +26,21 @@ i - left <= j when left >= 0, and j <= i + right when right >= 0.  Windows are
 inclusive on both ends; with causal the right side is additionally capped at
 i (so a (256, 256) window with causal sees keys [i-256, i]).
 
+Heads: k and v may carry fewer heads than q (multi-query attention, K/V
+shared across heads: "Flash Attention | Hermes Skill", Workflow 2, Step 3,
+q as [batch, seq, num_q_heads, dim] with k, v as [batch, seq, num_kv_heads,
+dim]).  The number of query heads must be a multiple of the number of K/V
+heads; see ``kv_head_of`` for which K/V head each query head reads.
+
 Readings where the pages say nothing (each listed in the design notes):
   * LSE is the natural-log logsumexp of the scaled, masked scores.
   * A row with no visible key gets O = 0 and LSE = -inf.  With Nq == Nk the
     diagonal key is always visible, so this does not arise for the GPU path.
   * Masks are aligned top-left (row i, key i on the diagonal).
   * fp8 inputs are dequantised as ``x_q * descale`` before anything else.
+  * With Hk K/V heads and Hq = g * Hk query heads, query heads form
+    contiguous groups of g: query head h reads K/V head h // g (one K/V head
+    for all query heads when Hk = 1).
 
 Work layout: rows are independent by definition, so they are processed in
 blocks; per block only keys inside the union of the rows' visible ranges are
@@ -48,6 +57,7 @@ from typing import Optional, Sequence, Tuple
 import numpy as np
 
 __all__ = [
+    "kv_head_of",
     "visible",
     "dequantize_e4m3",
     "attention_head",
@@ -58,6 +68,17 @@ __all__ = [
 
 # Upper bound on the number of float64 score elements materialised at once.
 _MAX_BLOCK_ELEMS = 1 << 24
+
+
+def kv_head_of(h: int, hq: int, hk: int) -> int:
+    """The K/V head that query head h reads when q has hq heads and k, v have hk.
+
+    Query heads form contiguous groups of hq // hk (the reading taken where
+    the pages only say that fewer K/V heads are shared across the heads).
+    """
+    if hk < 1 or hq % hk != 0:
+        raise ValueError(f"{hq} query heads cannot share {hk} K/V heads")
+    return h // (hq // hk)
 
 
 def visible(i, j, nk: int, causal: bool, window_left: int, window_right: int):
@@ -194,6 +215,8 @@ def attention(q, k, v, scale: Optional[float] = None, causal: bool = False,
               heads: Optional[Sequence[Tuple[int, int]]] = None):
     """Batched attention over 4-D arrays in ``layout`` ("bshd" or "bhsd").
 
+    k and v may have fewer heads than q (``kv_head_of``).
+
     Returns (O, LSE).  With ``heads=None`` and ``rows=None``: O in the input
     layout (float64) and LSE as [B, H, Nq].  With ``heads`` (a list of
     (b, h) pairs) and/or ``rows``: O as [len(heads), R, D] and LSE as
@@ -202,6 +225,10 @@ def attention(q, k, v, scale: Optional[float] = None, causal: bool = False,
     """
     qh, kh, vh = (_to_bhsd(np.asarray(x), layout) for x in (q, k, v))
     B, H, Nq, D = qh.shape
+    Hk = kh.shape[1]
+    if vh.shape[1] != Hk:
+        raise ValueError("k and v must have the same number of heads")
+    kv = [kv_head_of(h, H, Hk) for h in range(H)]
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     wl, wr = int(window[0]), int(window[1])
@@ -210,7 +237,7 @@ def attention(q, k, v, scale: Optional[float] = None, causal: bool = False,
         lse = np.empty((B, H, Nq), dtype=np.float64)
         for b in range(B):
             for h in range(H):
-                o[b, h], lse[b, h] = attention_head(qh[b, h], kh[b, h], vh[b, h], scale, causal, wl, wr)
+                o[b, h], lse[b, h] = attention_head(qh[b, h], kh[b, kv[h]], vh[b, kv[h]], scale, causal, wl, wr)
         if layout == "bshd":
             o = np.swapaxes(o, 1, 2)
         return o, lse
@@ -218,7 +245,7 @@ def attention(q, k, v, scale: Optional[float] = None, causal: bool = False,
         heads = [(b, h) for b in range(B) for h in range(H)]
     outs, lses = [], []
     for (b, h) in heads:
-        o1, l1 = attention_head(qh[b, h], kh[b, h], vh[b, h], scale, causal, wl, wr, rows)
+        o1, l1 = attention_head(qh[b, h], kh[b, kv[h]], vh[b, kv[h]], scale, causal, wl, wr, rows)
         outs.append(o1)
         lses.append(l1)
     return np.stack(outs), np.stack(lses)

@@ -268,6 +268,67 @@ def test_parallel_matches_serial():
 
 
 # ---------------------------------------------------------------------------
+# Fewer K/V heads than query heads (multi-query / grouped-query attention)
+# ---------------------------------------------------------------------------
+
+def _gqa_case(rng, B, H, Hk, N, D, layout):
+    shp = (B, N, H, D) if layout == "bshd" else (B, H, N, D)
+    shk = (B, N, Hk, D) if layout == "bshd" else (B, Hk, N, D)
+    return rng.standard_normal(shp), rng.standard_normal(shk), rng.standard_normal(shk)
+
+
+@pytest.mark.parametrize("hk", [1, 2, 3, 6])
+@pytest.mark.parametrize("layout", ["bshd", "bhsd"])
+@pytest.mark.parametrize("causal,wl,wr", [(False, -1, -1), (True, -1, -1), (True, 4, 0), (False, 3, 2)])
+def test_gqa_matches_mha_on_repeated_kv(hk, layout, causal, wl, wr):
+    # sharing a K/V head among a group of query heads is the same as giving
+    # every query head its own copy of that K/V head
+    rng = np.random.default_rng(40 + hk)
+    q, k, v = _gqa_case(rng, 2, 6, hk, 23, 8, layout)
+    ax = 2 if layout == "bshd" else 1
+    kr, vr = (np.repeat(x, 6 // hk, axis=ax) for x in (k, v))
+    o1, l1 = oracle.attention(q, k, v, 0.4, causal, (wl, wr), layout)
+    o2, l2 = oracle.attention(q, kr, vr, 0.4, causal, (wl, wr), layout)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+
+
+@pytest.mark.parametrize("hk", [1, 2, 4])
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_matches_torch_sdpa_fp64(hk, causal):
+    # torch's scaled_dot_product_attention with enable_gqa (float64, CPU)
+    rng = np.random.default_rng(50 + hk)
+    q, k, v = _gqa_case(rng, 2, 8, hk, 31, 16, "bhsd")
+    o, lse = oracle.attention(q, k, v, 0.3, causal, (-1, -1), "bhsd")
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        *(torch.from_numpy(x) for x in (q, k, v)), is_causal=causal, scale=0.3, enable_gqa=True).numpy()
+    np.testing.assert_allclose(o, ref, rtol=0, atol=1e-12)
+
+
+def test_gqa_head_counts():
+    assert [oracle.kv_head_of(h, 8, 2) for h in range(8)] == [0, 0, 0, 0, 1, 1, 1, 1]
+    assert [oracle.kv_head_of(h, 4, 1) for h in range(4)] == [0, 0, 0, 0]
+    with pytest.raises(ValueError):
+        oracle.kv_head_of(0, 6, 4)
+    rng = np.random.default_rng(3)
+    q, k, v = _gqa_case(rng, 1, 6, 4, 5, 4, "bshd")
+    with pytest.raises(ValueError):
+        oracle.attention(q, k, v, 0.5)
+
+
+def test_planted_gqa_interleaving_is_caught(monkeypatch):
+    # query head h reading K/V head h % Hk (interleaved groups) instead of
+    # h // (Hq / Hk) must fail the library pin
+    monkeypatch.setattr(sdpa_fp64, "kv_head_of", lambda h, hq, hk: h % hk)
+    rng = np.random.default_rng(51)
+    q, k, v = _gqa_case(rng, 1, 8, 2, 17, 8, "bhsd")
+    o, _ = sdpa_fp64.attention(q, k, v, 0.3, False, (-1, -1), "bhsd")
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        *(torch.from_numpy(x) for x in (q, k, v)), scale=0.3, enable_gqa=True).numpy()
+    assert not np.allclose(o, ref, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
 # Planted mistakes: each variant of the oracle carries one plausible bug; the
 # pins above must reject it.  The bugs live only in these test doubles.
 # ---------------------------------------------------------------------------
