@@ -58,8 +58,9 @@ def workload_flops(w) -> float:
 def workload_bytes(w) -> float:
     """One read of Q, K, V plus one write of O (16-bit) and of the fp32 LSE."""
     esz = 1 if w.dtype == "fp8" else 2
-    elems = w.batch * w.heads * w.seqlen * w.headdim
-    return float(3 * elems * esz + 2 * elems + 4 * w.batch * w.heads * w.seqlen)
+    q_elems = w.batch * w.heads * w.seqlen * w.headdim
+    kv_elems = w.batch * w.kv_heads * w.seqlen * w.headdim
+    return float((q_elems + 2 * kv_elems) * esz + 2 * q_elems + 4 * w.batch * w.heads * w.seqlen)
 
 
 def kernel_hash() -> str:
@@ -138,8 +139,9 @@ def cpu_baseline(w, target_s: float = 12.0, max_procs: int = 16):
 
     def head(b, h):
         out = []
-        for t, s in zip((inp.q, inp.k, inp.v), inp.descale):
-            x = t[b, :, h, :] if w.layout == "bshd" else t[b, h, :, :]
+        g = oracle.kv_head_of(h, w.heads, w.kv_heads)   # the K/V head query head h reads
+        for t, s, hh in zip((inp.q, inp.k, inp.v), inp.descale, (h, g, g)):
+            x = t[b, :, hh, :] if w.layout == "bshd" else t[b, hh, :, :]
             if x.dtype == torch.float8_e4m3fn:
                 out.append(oracle.dequantize_e4m3(x.contiguous().view(torch.uint8).numpy(), s))
             else:
@@ -215,7 +217,7 @@ def main(argv=None):
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {
-            "workload": name, "batch": w.batch, "heads": w.heads, "seqlen": w.seqlen, "headdim": w.headdim,
+            "workload": name, "batch": w.batch, "heads": w.heads, "kv_heads": w.kv_heads, "seqlen": w.seqlen, "headdim": w.headdim,
             "causal": w.causal, "window": [w.window_left, w.window_right], "layout": w.layout,
             "softmax_scale": w.softmax_scale,
         },

@@ -81,7 +81,7 @@ int validate(const ea_attn_args* a, bool* empty) {
   if (a->headdim != 64 && a->headdim != 128) return EA_EUNSUPPORTED;
   if (fp8 && a->headdim != 128) return EA_EUNSUPPORTED;
   if (a->seqlen_q != a->seqlen_k) return EA_EUNSUPPORTED;
-  if (a->nheads_q != a->nheads_k) return EA_EUNSUPPORTED;
+  if (a->nheads_q % a->nheads_k != 0) return EA_EUNSUPPORTED;
   if (!(a->softmax_scale > 0.f)) return EA_EUNSUPPORTED;
 
   if (a->batch == 0 || a->seqlen_q == 0) {
@@ -90,7 +90,7 @@ int validate(const ea_attn_args* a, bool* empty) {
   }
   if (a->q == nullptr || a->k == nullptr || a->v == nullptr || a->o == nullptr) return EA_EINVAL;
 
-  const int64_t B = a->batch, N = a->seqlen_q, H = a->nheads_q, D = a->headdim;
+  const int64_t B = a->batch, N = a->seqlen_q, H = a->nheads_q, Hk = a->nheads_k, D = a->headdim;
   const int ein = elem_bytes(a->in_dtype), eout = elem_bytes(a->out_dtype);
   const int64_t strides[12] = {a->q_stride_b, a->q_stride_s, a->q_stride_h, a->k_stride_b, a->k_stride_s, a->k_stride_h,
                                a->v_stride_b, a->v_stride_s, a->v_stride_h, a->o_stride_b, a->o_stride_s, a->o_stride_h};
@@ -114,8 +114,8 @@ int validate(const ea_attn_args* a, bool* empty) {
 
   const Span so = span_of(a->o, B, N, H, D, a->o_stride_b, a->o_stride_s, a->o_stride_h, eout);
   const Span sq = span_of(a->q, B, N, H, D, a->q_stride_b, a->q_stride_s, a->q_stride_h, ein);
-  const Span sk = span_of(a->k, B, N, H, D, a->k_stride_b, a->k_stride_s, a->k_stride_h, ein);
-  const Span sv = span_of(a->v, B, N, H, D, a->v_stride_b, a->v_stride_s, a->v_stride_h, ein);
+  const Span sk = span_of(a->k, B, N, Hk, D, a->k_stride_b, a->k_stride_s, a->k_stride_h, ein);
+  const Span sv = span_of(a->v, B, N, Hk, D, a->v_stride_b, a->v_stride_s, a->v_stride_h, ein);
   if (overlaps(so, sq) || overlaps(so, sk) || overlaps(so, sv)) return EA_EINVAL;
   return EA_OK;
 }
@@ -132,6 +132,7 @@ ea::FwdParams make_params(const ea_attn_args* a, int cfg) {
   p.lse = a->lse;
   p.batch = (int)a->batch;
   p.heads = (int)a->nheads_q;
+  p.group = (int)(a->nheads_q / a->nheads_k);
   p.n = (int)a->seqlen_q;
   p.q_tiles = (p.n + ea::tile_bm(cfg) - 1) / ea::tile_bm(cfg);
   p.q_sb = a->q_stride_b; p.q_ss = a->q_stride_s; p.q_sh = a->q_stride_h;

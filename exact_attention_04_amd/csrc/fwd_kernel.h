@@ -13,6 +13,7 @@ struct FwdParams {
   void* o;
   float* lse;            // may be null
   int batch, heads, n, q_tiles;
+  int group;             // query heads per K/V head (query head h reads K/V head h / group)
   int64_t q_sb, q_ss, q_sh;
   int64_t k_sb, k_ss, k_sh;
   int64_t v_sb, v_ss, v_sh;

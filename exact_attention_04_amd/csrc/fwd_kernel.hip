@@ -295,18 +295,26 @@ attn_fwd_kernel(const FwdParams p) {
 
   // ---- work assignment: heaviest query tiles first (causal tiles near the
   // end of the sequence see the most keys), all heads of one tile index
-  // together.
+  // together.  Workgroups go to the 8 XCDs round robin (workgroup w on XCD
+  // w % 8), so with K/V heads shared by groups of query heads the (batch,
+  // head) order is permuted to put each whole group on one XCD, where its
+  // K/V stays in that XCD's L2.
   const int bh_count = p.batch * p.heads;
   const int tile = p.q_tiles - 1 - (int)(blockIdx.x / bh_count);
-  const int bh = (int)(blockIdx.x % bh_count);
+  int bh = (int)(blockIdx.x % bh_count);
+  if (p.group > 1 && bh_count % (8 * p.group) == 0) {
+    const int x = bh & 7, y = bh >> 3;
+    bh = ((y / p.group) * 8 + x) * p.group + y % p.group;
+  }
   const int b = bh / p.heads;
   const int h = bh - b * p.heads;
+  const int hkv = h / p.group;      // the K/V head this query head reads
   const int q0 = tile * kBM;
   const int n = p.n;
 
   const unsigned char* qg = (const unsigned char*)p.q + ((int64_t)b * p.q_sb + (int64_t)h * p.q_sh) * C::kInBytes;
-  const unsigned char* kg = (const unsigned char*)p.k + ((int64_t)b * p.k_sb + (int64_t)h * p.k_sh) * C::kInBytes;
-  const unsigned char* vg = (const unsigned char*)p.v + ((int64_t)b * p.v_sb + (int64_t)h * p.v_sh) * C::kInBytes;
+  const unsigned char* kg = (const unsigned char*)p.k + ((int64_t)b * p.k_sb + (int64_t)hkv * p.k_sh) * C::kInBytes;
+  const unsigned char* vg = (const unsigned char*)p.v + ((int64_t)b * p.v_sb + (int64_t)hkv * p.v_sh) * C::kInBytes;
   const int k_row_stride = (int)(p.k_ss * C::kInBytes);   // bytes; < 2^31 (checked by the host)
   const int v_row_stride = (int)(p.v_ss * C::kInBytes);
 

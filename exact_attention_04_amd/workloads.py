@@ -8,7 +8,8 @@ Quick start and Workflows 1-3); the workloads below keep that distribution.
 
 Recipe (fixed so that a run can be reproduced anywhere):
   * ``numpy.random.default_rng(seed)``; draw q, then k, then v, each a float32
-    standard normal array in the workload's layout shape.
+    standard normal array in the workload's layout shape (k and v with the
+    workload's K/V head count, which may be smaller than q's).
   * 16-bit workloads: cast round-to-nearest-even through torch on the CPU.
   * fp8 workloads: per-tensor scale ``s = amax|x| / 448`` in float32, then
     ``x / s`` cast round-to-nearest-even to OCP float8 e4m3fn (torch CPU).  The
@@ -41,6 +42,7 @@ class Workload:
     window_right: int = -1
     scale: Optional[float] = None
     seed: int = 1000
+    heads_kv: Optional[int] = None   # K/V heads (fewer than `heads`: shared K/V)
 
     @property
     def softmax_scale(self) -> float:
@@ -50,10 +52,15 @@ class Workload:
     def out_dtype(self) -> str:
         return "bf16" if self.dtype == "fp8" else self.dtype
 
-    def shape(self) -> Tuple[int, int, int, int]:
+    @property
+    def kv_heads(self) -> int:
+        return self.heads if self.heads_kv is None else self.heads_kv
+
+    def shape(self, heads: Optional[int] = None) -> Tuple[int, int, int, int]:
+        h = self.heads if heads is None else heads
         if self.layout == "bshd":
-            return (self.batch, self.seqlen, self.heads, self.headdim)
-        return (self.batch, self.heads, self.seqlen, self.headdim)
+            return (self.batch, self.seqlen, h, self.headdim)
+        return (self.batch, h, self.seqlen, self.headdim)
 
 
 # The five workloads.  Indices match the order the targets list them in.
@@ -74,6 +81,15 @@ WORKLOADS = {
 }
 
 HEADLINE = "sdpa_b4h32n4096d128_bf16_causal"
+
+# Beyond the five: the headline shape with K/V shared by groups of 4 query
+# heads (8 K/V heads), and by all 32 (one K/V head).
+WORKLOADS["gqa_b4h32kv8n4096d128_bf16_causal"] = Workload(
+    "gqa_b4h32kv8n4096d128_bf16_causal", 4, 32, 4096, 128, "bf16", "bshd", True,
+    scale=1.0 / math.sqrt(128.0), seed=1005, heads_kv=8)
+WORKLOADS["mqa_b4h32kv1n4096d128_bf16_causal"] = Workload(
+    "mqa_b4h32kv1n4096d128_bf16_causal", 4, 32, 4096, 128, "bf16", "bshd", True,
+    scale=1.0 / math.sqrt(128.0), seed=1006, heads_kv=1)
 
 
 @dataclasses.dataclass
@@ -106,9 +122,10 @@ def quantize_e4m3_per_tensor(x: np.ndarray) -> Tuple[torch.Tensor, float]:
     return q, float(s)
 
 
-def make_inputs_shape(shape, dtype: str, seed: int) -> Inputs:
+def make_inputs_shape(shape, dtype: str, seed: int, kv_shape=None) -> Inputs:
     rng = np.random.default_rng(seed)
-    arrs = [rng.standard_normal(size=shape, dtype=np.float32) for _ in range(3)]
+    kv_shape = shape if kv_shape is None else kv_shape
+    arrs = [rng.standard_normal(size=s, dtype=np.float32) for s in (shape, kv_shape, kv_shape)]
     if dtype == "fp8":
         qs = [quantize_e4m3_per_tensor(a) for a in arrs]
         return Inputs(qs[0][0], qs[1][0], qs[2][0], (qs[0][1], qs[1][1], qs[2][1]))
@@ -118,9 +135,10 @@ def make_inputs_shape(shape, dtype: str, seed: int) -> Inputs:
 
 
 def make_inputs(w: Workload) -> Inputs:
-    return make_inputs_shape(w.shape(), w.dtype, w.seed)
+    return make_inputs_shape(w.shape(), w.dtype, w.seed, w.shape(w.kv_heads))
 
 
-def small_case(batch, heads, seqlen, headdim, dtype, layout, seed) -> Inputs:
-    shape = (batch, seqlen, heads, headdim) if layout == "bshd" else (batch, heads, seqlen, headdim)
-    return make_inputs_shape(shape, dtype, seed)
+def small_case(batch, heads, seqlen, headdim, dtype, layout, seed, heads_kv=None) -> Inputs:
+    def shp(h):
+        return (batch, seqlen, h, headdim) if layout == "bshd" else (batch, h, seqlen, headdim)
+    return make_inputs_shape(shp(heads), dtype, seed, shp(heads if heads_kv is None else heads_kv))

@@ -79,11 +79,15 @@ typedef struct ea_attn_args {
   int64_t seqlen_q;          /* Nq >= 0 */
   int64_t seqlen_k;          /* Nk >= 0; this version requires Nq == Nk */
   int64_t nheads_q;          /* Hq >= 1 */
-  int64_t nheads_k;          /* Hk >= 1; this version requires Hk == Hq */
+  int64_t nheads_k;          /* Hk >= 1 K/V heads; Hq must be a multiple of Hk.
+                                With Hk < Hq the K/V heads are shared (multi-query
+                                / grouped-query attention, "Flash Attention |
+                                Hermes Skill", Workflow 2, Step 3): query head h
+                                reads K/V head h / (Hq / Hk) */
   int64_t headdim;           /* D: 64 or 128 */
   const void* q;             /* [B, Nq, Hq, D] via the strides below */
   const void* k;             /* [B, Nk, Hk, D] */
-  const void* v;             /* [B, Nk, Hk, D] */
+  const void* v;             /* [B, Nk, Hk, D] (same strides rules as k) */
   void* o;                   /* [B, Nq, Hq, D], written in full */
   float* lse;                /* [B, Hq, Nq] float32, natural log of the scaled,
                                 masked scores; NULL = do not write */
@@ -120,7 +124,7 @@ typedef struct ea_attn_plan_info {
  *                    and > 0, or != 1 for 16-bit inputs; window bounds < -1;
  *                    o overlapping q, k or v.
  *   EA_EUNSUPPORTED  float32 inputs; headdim not 64 or 128 (fp8: not 128);
- *                    Nq != Nk; Hq != Hk; softmax_scale <= 0; an output
+ *                    Nq != Nk; Hq not a multiple of Hk; softmax_scale <= 0; an output
  *                    dtype other than the one above; a negative stride; a
  *                    base pointer not 16-byte aligned or a b/s/h stride
  *                    whose byte size is not a multiple of 16 (the kernels

@@ -109,9 +109,14 @@ def sampled_check(inp: Inputs, dtype: str, o_gpu: torch.Tensor, lse_gpu: torch.T
     def head_arr(t, s, b, h):
         x = t[b, :, h, :] if layout == "bshd" else t[b, h, :, :]
         return stored_f64(x.contiguous(), s)
+    hax = 2 if layout == "bshd" else 1
+    hq, hk = inp.q.shape[hax], inp.k.shape[hax]
     o_refs, l_refs = [], []
     for (b, h) in heads:
-        qf, kf, vf = (head_arr(t, s, b, h) for t, s in zip((inp.q, inp.k, inp.v), inp.descale))
+        g = oracle.kv_head_of(h, hq, hk)   # the K/V head query head h reads
+        qf = head_arr(inp.q, inp.descale[0], b, h)
+        kf = head_arr(inp.k, inp.descale[1], b, g)
+        vf = head_arr(inp.v, inp.descale[2], b, g)
         sc = 1.0 / math.sqrt(qf.shape[-1]) if scale is None else scale
         o1, l1 = oracle.attention_head(qf, kf, vf, sc, causal, window[0], window[1], rows=rows)
         o_refs.append(o1)

@@ -139,7 +139,7 @@ def test_plan_tile_counts_causal_and_window():
     ("in_dtype", _lib.EA_F32, _lib.EA_EUNSUPPORTED),  # fp32 input
     ("headdim", 96, _lib.EA_EUNSUPPORTED),
     ("seqlen_k", 299, _lib.EA_EUNSUPPORTED),
-    ("nheads_k", 1, _lib.EA_EUNSUPPORTED),
+    ("nheads_k", 2, _lib.EA_EUNSUPPORTED),         # 3 query heads cannot share 2 K/V heads
     ("out_dtype", _lib.EA_F16, _lib.EA_EUNSUPPORTED),
     ("softmax_scale", -0.5, _lib.EA_EUNSUPPORTED),
     ("q", FAKE + 8, _lib.EA_EUNSUPPORTED),          # not 16-byte aligned
@@ -154,6 +154,19 @@ def test_validation_errors(field, value, code):
     assert st == code, (field, value, _lib.status_string(st))
     # the launch entry point applies the same checks before touching a device
     assert _lib.lib().ea_attn_fwd(ctypes.byref(a), None) == code
+
+
+def test_shared_kv_heads():
+    # query heads sharing K/V heads: any Hk that divides Hq
+    for hk in (1, 2, 4, 8):
+        a = make(H=8, nheads_k=hk)
+        for t in "kv":   # K/V tensors with hk heads (BSHD strides)
+            setattr(a, f"{t}_stride_b", 300 * hk * 128)
+            setattr(a, f"{t}_stride_s", hk * 128)
+        st, info = plan_status(a)
+        assert st == _lib.EA_OK, (hk, _lib.status_string(st))
+        assert info.grid == 2 * 8 * math.ceil(300 / 128)
+    assert plan_status(make(H=8, nheads_k=3))[0] == _lib.EA_EUNSUPPORTED
 
 
 def test_fp8_argument_rules():

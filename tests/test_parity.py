@@ -90,6 +90,40 @@ def test_workload_sampled(name):
     print(name, r)
 
 
+# ---------------------------------------------------------------------------
+# K/V heads shared by groups of query heads
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("heads,heads_kv", [(8, 2), (6, 3), (4, 1), (16, 4)])
+@pytest.mark.parametrize("mask", ["none", "causal", "w17_5"])
+@pytest.mark.parametrize("layout", ["bshd", "bhsd"])
+def test_shared_kv_heads(heads, heads_kv, mask, layout):
+    causal, window = MASKS[mask]
+    inp = small_case(2, heads, 333, 128, "bf16", layout, 60 + heads + heads_kv, heads_kv=heads_kv)
+    full_check(inp, "bf16", causal=causal, window=window, layout=layout,
+               what=f"H{heads}/Hk{heads_kv} {mask} {layout}")
+
+
+@pytest.mark.parametrize("dtype,d", [("f16", 64), ("fp8", 128)])
+def test_shared_kv_heads_other_types(dtype, d):
+    inp = small_case(1, 8, 300, d, dtype, "bshd", 71, heads_kv=2)
+    full_check(inp, dtype, causal=True, what=f"{dtype} d{d} H8/Hk2")
+
+
+@pytest.mark.parametrize("name", ["gqa_b4h32kv8n4096d128_bf16_causal", "mqa_b4h32kv1n4096d128_bf16_causal"])
+def test_shared_kv_workload_sampled(name):
+    w = WORKLOADS[name]
+    inp = make_inputs(w)
+    o, lse = run_gpu(inp, causal=w.causal, scale=w.softmax_scale, layout=w.layout)
+    assert torch.isfinite(o.float()).all().item()
+    rng = np.random.default_rng(w.seed)
+    heads = [(0, 0), (w.batch - 1, w.heads - 1), (1, 5), (2, 30)]
+    heads += [(int(rng.integers(w.batch)), int(rng.integers(w.heads))) for _ in range(2)]
+    r = sampled_check(inp, w.dtype, o, lse, heads, sample_rows(w.seqlen, w.seed), causal=w.causal,
+                      scale=w.softmax_scale, layout=w.layout, what=name)
+    print(name, r)
+
+
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("scale", [1.0, 2.0])

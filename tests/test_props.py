@@ -54,6 +54,22 @@ def test_deterministic_many_workgroups(shape, dtype, causal, window):
         assert _same(o1, o2) and torch.equal(l1, l2)
 
 
+@pytest.mark.parametrize("heads,heads_kv", [(32, 8), (8, 1), (16, 16)])
+def test_shared_kv_equals_repeated_kv_bitwise(heads, heads_kv):
+    # a query head reading a shared K/V head computes exactly what it computes
+    # with its own copy of that head: the same bits, at a size with many
+    # workgroups per XCD (where the work order groups the sharing heads)
+    g = torch.Generator(device="cuda").manual_seed(12)
+    q = torch.randn((2, 1500, heads, 128), device="cuda", generator=g).to(torch.bfloat16)
+    k, v = (torch.randn((2, 1500, heads_kv, 128), device="cuda", generator=g).to(torch.bfloat16) for _ in range(2))
+    o1, l1 = attention(q, k, v, causal=True)
+    rep = heads // heads_kv
+    kr, vr = (x.repeat_interleave(rep, dim=2).contiguous() for x in (k, v))
+    o2, l2 = attention(q, kr, vr, causal=True)
+    torch.cuda.synchronize()
+    assert _same(o1, o2) and torch.equal(l1, l2)
+
+
 def test_layouts_bitwise_equal():
     q, k, v = _gpu(small_case(2, 3, 300, 128, "bf16", "bshd", 2))
     o1, l1 = attention(q, k, v, causal=True, layout="bshd")
