@@ -17,3 +17,4 @@ from .sdpa_fp64 import (  # noqa: F401
     kv_head_of,
     visible,
 )
+from .sdpa_bwd_fp64 import attention_backward, attention_backward_head  # noqa: F401
