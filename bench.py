@@ -35,7 +35,8 @@ METRIC = "attention fwd TFLOP/s and % of MFMA peak (bf16 causal d=128, N=4096)"
 # MI355X dense MFMA peaks (256 CUs x 2.4 GHz): 16-bit 4096 flop/CU/clk, fp8 8192.
 PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "fp8": 5033.2}
 HBM_PEAK_GBS = 8000.0
-KERNEL_SRC = os.path.join(ROOT, "exact_attention_04_amd", "csrc", "fwd_kernel.hip")
+# the forward kernel's sources (a recorded traffic measurement is valid only for these)
+KERNEL_SRCS = [os.path.join(ROOT, "exact_attention_04_amd", "csrc", f) for f in ("fwd_kernel.hip", "kernel_common.h")]
 
 
 def visible_pairs_per_head(w) -> int:
@@ -64,8 +65,11 @@ def workload_bytes(w) -> float:
 
 
 def kernel_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload: str):

@@ -15,10 +15,10 @@ LIB_PATH = os.path.join(PKG_DIR, "libea_attn.so")
 
 EA_OK, EA_EINVAL, EA_EUNSUPPORTED, EA_EDEVICE, EA_EHIP = 0, 1, 2, 3, 4
 EA_F16, EA_BF16, EA_FP8_E4M3, EA_F32 = 1, 2, 3, 4
-EA_ABI_VERSION = 1
+EA_ABI_VERSION = 2
 
 # Every symbol the header declares.
-EXPORTS = ("ea_attn_fwd", "ea_attn_plan", "ea_status_string", "ea_last_hip_error", "ea_abi_version")
+EXPORTS = ("ea_attn_fwd", "ea_attn_bwd", "ea_attn_plan", "ea_status_string", "ea_last_hip_error", "ea_abi_version")
 
 
 class AttnArgs(ctypes.Structure):
@@ -50,6 +50,30 @@ class AttnArgs(ctypes.Structure):
         ("v_stride_b", ctypes.c_int64), ("v_stride_s", ctypes.c_int64), ("v_stride_h", ctypes.c_int64),
         ("o_stride_b", ctypes.c_int64), ("o_stride_s", ctypes.c_int64), ("o_stride_h", ctypes.c_int64),
         ("lse_stride_b", ctypes.c_int64), ("lse_stride_h", ctypes.c_int64),
+    ]
+
+
+class BwdArgs(ctypes.Structure):
+    """Mirror of ``ea_attn_bwd_args``."""
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("dtype", ctypes.c_int32),
+        ("causal", ctypes.c_int32),
+        ("window_left", ctypes.c_int32),
+        ("window_right", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float),
+        ("batch", ctypes.c_int64),
+        ("seqlen", ctypes.c_int64),
+        ("nheads_q", ctypes.c_int64),
+        ("nheads_k", ctypes.c_int64),
+        ("headdim", ctypes.c_int64),
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("o", ctypes.c_void_p), ("dout", ctypes.c_void_p),
+        ("lse", ctypes.c_void_p), ("delta", ctypes.c_void_p),
+        ("dq", ctypes.c_void_p), ("dk", ctypes.c_void_p), ("dv", ctypes.c_void_p),
+    ] + [(f"{t}_stride_{a}", ctypes.c_int64) for t in ("q", "k", "v", "o", "do", "dq", "dk", "dv") for a in "bsh"] + [
+        ("lse_stride_b", ctypes.c_int64), ("lse_stride_h", ctypes.c_int64),
+        ("delta_stride_b", ctypes.c_int64), ("delta_stride_h", ctypes.c_int64),
     ]
 
 
@@ -86,6 +110,8 @@ def lib() -> ctypes.CDLL:
             h = ctypes.CDLL(LIB_PATH)
             h.ea_attn_fwd.argtypes = [ctypes.POINTER(AttnArgs), ctypes.c_void_p]
             h.ea_attn_fwd.restype = ctypes.c_int
+            h.ea_attn_bwd.argtypes = [ctypes.POINTER(BwdArgs), ctypes.c_void_p]
+            h.ea_attn_bwd.restype = ctypes.c_int
             h.ea_attn_plan.argtypes = [ctypes.POINTER(AttnArgs), ctypes.POINTER(PlanInfo)]
             h.ea_attn_plan.restype = ctypes.c_int
             h.ea_status_string.argtypes = [ctypes.c_int]
@@ -130,6 +156,10 @@ def check(code: int) -> None:
 
 def fwd(args: AttnArgs, stream: int) -> int:
     return lib().ea_attn_fwd(ctypes.byref(args), ctypes.c_void_p(stream))
+
+
+def bwd(args: BwdArgs, stream: int) -> int:
+    return lib().ea_attn_bwd(ctypes.byref(args), ctypes.c_void_p(stream))
 
 
 def plan(args: AttnArgs) -> PlanInfo:

@@ -109,3 +109,53 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool
 def plan(q, k, v, o, lse=None, **kw) -> _lib.PlanInfo:
     """The tile configuration ``attention`` would launch (no device work)."""
     return _lib.plan(make_args(q, k, v, o, lse, **kw))
+
+
+def attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, dout: torch.Tensor,
+                       lse: torch.Tensor, *, causal: bool = False, window_size: Tuple[int, int] = (-1, -1),
+                       softmax_scale: Optional[float] = None, layout: str = "bshd",
+                       dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+                       dv: Optional[torch.Tensor] = None, delta: Optional[torch.Tensor] = None):
+    """Gradients of attention on the current HIP stream (16-bit inputs).
+
+    ``o`` and ``lse`` are the forward's outputs for the same arguments and
+    ``dout`` the gradient with respect to ``o``.  Returns ``(dq, dk, dv,
+    delta)``: dq, dk, dv shaped like q, k, v; delta = rowsum(dout * o) as
+    float32 [B, H, N].  Raises ValueError for arguments the library rejects.
+    """
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("lse", lse)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor (this library has no CPU path)")
+    if q.dtype not in (torch.float16, torch.bfloat16) or any(t.dtype != q.dtype for t in (k, v, o, dout)):
+        raise ValueError("the backward takes float16 or bfloat16 q, k, v, o, dout of one dtype")
+    (B, N, H, D), (qb, qs, qh) = _dims(q, layout)
+    (Bk, Nk, Hk, Dk), (kb, ks, kh) = _dims(k, layout)
+    if Bk != B or Nk != N or Dk != D or tuple(v.shape) != tuple(k.shape) or tuple(o.shape) != tuple(q.shape) \
+            or tuple(dout.shape) != tuple(q.shape) or tuple(lse.shape) != (B, H, N):
+        raise ValueError("shape mismatch between q, k, v, o, dout, lse")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if delta is None else delta
+    a = _lib.BwdArgs()
+    a.struct_size = _lib.ctypes.sizeof(_lib.BwdArgs)
+    a.dtype = _DTYPES[q.dtype]
+    a.causal = 1 if causal else 0
+    a.window_left, a.window_right = int(window_size[0]), int(window_size[1])
+    a.softmax_scale = float(1.0 / math.sqrt(D) if softmax_scale is None else softmax_scale)
+    a.batch, a.seqlen, a.nheads_q, a.nheads_k, a.headdim = B, N, H, Hk, D
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+        _, (sb, ss, sh) = _dims(t, layout)
+        setattr(a, f"{name}_stride_b", sb)
+        setattr(a, f"{name}_stride_s", ss)
+        setattr(a, f"{name}_stride_h", sh)
+    a.q, a.k, a.v, a.o, a.dout = q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr()
+    a.dq, a.dk, a.dv = dq.data_ptr(), dk.data_ptr(), dv.data_ptr()
+    a.lse, a.delta = lse.data_ptr(), delta.data_ptr()
+    if lse.stride(2) != 1 or delta.stride(2) != 1:
+        raise ValueError("lse and delta rows must be contiguous")
+    a.lse_stride_b, a.lse_stride_h = lse.stride(0), lse.stride(1)
+    a.delta_stride_b, a.delta_stride_h = delta.stride(0), delta.stride(1)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    _lib.check(_lib.bwd(a, stream))
+    return dq, dk, dv, delta

@@ -9,6 +9,7 @@
 #include <mutex>
 
 #include "ea_attn.h"
+#include "bwd_kernel.h"
 #include "fwd_kernel.h"
 
 namespace {
@@ -151,6 +152,106 @@ ea::FwdParams make_params(const ea_attn_args* a, int cfg) {
   return p;
 }
 
+// Span of an fp32 [B, H, N] array with row stride 1.
+Span span_rows_f32(const void* base, int64_t B, int64_t H, int64_t N, int64_t sb, int64_t sh) {
+  const uintptr_t lo = (uintptr_t)base;
+  return Span{lo, lo + (uintptr_t)(((B - 1) * sb + (H - 1) * sh + N) * 4)};
+}
+
+// Checks of ea_attn_bwd.  Returns EA_OK, or the error; sets *empty when there
+// is nothing to compute.
+int validate_bwd(const ea_attn_bwd_args* a, bool* empty) {
+  *empty = false;
+  if (a == nullptr || a->struct_size < sizeof(ea_attn_bwd_args)) return EA_EINVAL;
+  if (a->batch < 0 || a->seqlen < 0 || a->nheads_q < 1 || a->nheads_k < 1 || a->headdim < 1) return EA_EINVAL;
+  if (elem_bytes(a->dtype) == 0) return EA_EINVAL;
+  if (!std::isfinite(a->softmax_scale)) return EA_EINVAL;
+  if (a->window_left < -1 || a->window_right < -1) return EA_EINVAL;
+  if (a->dtype != EA_F16 && a->dtype != EA_BF16) return EA_EUNSUPPORTED;
+  if (a->headdim != 64 && a->headdim != 128) return EA_EUNSUPPORTED;
+  if (a->nheads_q % a->nheads_k != 0) return EA_EUNSUPPORTED;
+  if (!(a->softmax_scale > 0.f)) return EA_EUNSUPPORTED;
+  if (a->batch == 0 || a->seqlen == 0) {
+    *empty = true;
+    return EA_OK;
+  }
+  const void* ptrs[10] = {a->q, a->k, a->v, a->o, a->dout, a->lse, a->delta, a->dq, a->dk, a->dv};
+  for (int i = 0; i < 10; ++i)
+    if (ptrs[i] == nullptr) return EA_EINVAL;
+
+  const int64_t B = a->batch, N = a->seqlen, H = a->nheads_q, Hk = a->nheads_k, D = a->headdim;
+  const int64_t strides[24] = {a->q_stride_b,  a->q_stride_s,  a->q_stride_h,  a->k_stride_b,  a->k_stride_s,  a->k_stride_h,
+                               a->v_stride_b,  a->v_stride_s,  a->v_stride_h,  a->o_stride_b,  a->o_stride_s,  a->o_stride_h,
+                               a->do_stride_b, a->do_stride_s, a->do_stride_h, a->dq_stride_b, a->dq_stride_s, a->dq_stride_h,
+                               a->dk_stride_b, a->dk_stride_s, a->dk_stride_h, a->dv_stride_b, a->dv_stride_s, a->dv_stride_h};
+  for (int i = 0; i < 24; ++i) {
+    if (strides[i] < 0) return EA_EUNSUPPORTED;
+    if ((strides[i] * 2) % 16 != 0) return EA_EUNSUPPORTED;
+  }
+  for (int i = 0; i < 10; ++i) {
+    if (i == 5 || i == 6) continue;
+    if (!aligned16(ptrs[i])) return EA_EUNSUPPORTED;
+  }
+  if (((uintptr_t)a->lse & 3u) != 0 || ((uintptr_t)a->delta & 3u) != 0) return EA_EUNSUPPORTED;
+  if (a->lse_stride_b < 0 || a->lse_stride_h < 0 || a->delta_stride_b < 0 || a->delta_stride_h < 0)
+    return EA_EUNSUPPORTED;
+  const int64_t lim = (int64_t)1 << 31;
+  if (N >= lim / 2 || B * H >= lim) return EA_EUNSUPPORTED;
+  if ((N + 127) / 128 * B * H >= lim / 2) return EA_EUNSUPPORTED;
+  for (int i = 0; i < 8; ++i) {
+    if (strides[3 * i + 1] * N >= lim) return EA_EUNSUPPORTED;
+    if (strides[3 * i + 1] * 64 * 2 >= lim) return EA_EUNSUPPORTED;
+  }
+  // outputs (dq, dk, dv, delta) overlap neither each other nor any input
+  const Span in[6] = {span_of(a->q, B, N, H, D, a->q_stride_b, a->q_stride_s, a->q_stride_h, 2),
+                      span_of(a->k, B, N, Hk, D, a->k_stride_b, a->k_stride_s, a->k_stride_h, 2),
+                      span_of(a->v, B, N, Hk, D, a->v_stride_b, a->v_stride_s, a->v_stride_h, 2),
+                      span_of(a->o, B, N, H, D, a->o_stride_b, a->o_stride_s, a->o_stride_h, 2),
+                      span_of(a->dout, B, N, H, D, a->do_stride_b, a->do_stride_s, a->do_stride_h, 2),
+                      span_rows_f32(a->lse, B, H, N, a->lse_stride_b, a->lse_stride_h)};
+  const Span out[4] = {span_of(a->dq, B, N, H, D, a->dq_stride_b, a->dq_stride_s, a->dq_stride_h, 2),
+                       span_of(a->dk, B, N, Hk, D, a->dk_stride_b, a->dk_stride_s, a->dk_stride_h, 2),
+                       span_of(a->dv, B, N, Hk, D, a->dv_stride_b, a->dv_stride_s, a->dv_stride_h, 2),
+                       span_rows_f32(a->delta, B, H, N, a->delta_stride_b, a->delta_stride_h)};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(out[i], in[j])) return EA_EINVAL;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(out[i], out[j])) return EA_EINVAL;
+  }
+  return EA_OK;
+}
+
+ea::BwdParams make_bwd_params(const ea_attn_bwd_args* a) {
+  ea::BwdParams p;
+  p.q = a->q; p.k = a->k; p.v = a->v; p.o = a->o; p.dout = a->dout;
+  p.lse = a->lse; p.delta = a->delta;
+  p.dq = a->dq; p.dk = a->dk; p.dv = a->dv;
+  p.batch = (int)a->batch;
+  p.heads = (int)a->nheads_q;
+  p.heads_kv = (int)a->nheads_k;
+  p.group = (int)(a->nheads_q / a->nheads_k);
+  p.n = (int)a->seqlen;
+  p.q_tiles = (p.n + 127) / 128;
+  p.k_blocks = (p.n + 127) / 128;
+  p.q_sb = a->q_stride_b; p.q_ss = a->q_stride_s; p.q_sh = a->q_stride_h;
+  p.k_sb = a->k_stride_b; p.k_ss = a->k_stride_s; p.k_sh = a->k_stride_h;
+  p.v_sb = a->v_stride_b; p.v_ss = a->v_stride_s; p.v_sh = a->v_stride_h;
+  p.o_sb = a->o_stride_b; p.o_ss = a->o_stride_s; p.o_sh = a->o_stride_h;
+  p.do_sb = a->do_stride_b; p.do_ss = a->do_stride_s; p.do_sh = a->do_stride_h;
+  p.dq_sb = a->dq_stride_b; p.dq_ss = a->dq_stride_s; p.dq_sh = a->dq_stride_h;
+  p.dk_sb = a->dk_stride_b; p.dk_ss = a->dk_stride_s; p.dk_sh = a->dk_stride_h;
+  p.dv_sb = a->dv_stride_b; p.dv_ss = a->dv_stride_s; p.dv_sh = a->dv_stride_h;
+  p.lse_sb = a->lse_stride_b; p.lse_sh = a->lse_stride_h;
+  p.delta_sb = a->delta_stride_b; p.delta_sh = a->delta_stride_h;
+  p.causal = a->causal ? 1 : 0;
+  p.wl = a->window_left;
+  p.wr = a->window_right;
+  p.scale = a->softmax_scale;
+  p.c_log2 = (float)((double)a->softmax_scale * 1.4426950408889634);
+  return p;
+}
+
 // Host-side mirror of the kernel's tile walk, for plan reports only.
 void count_tiles(const ea::FwdParams& p, int cfg, int64_t* tiles, int64_t* masked) {
   const int bm = ea::tile_bm(cfg), bn = ea::tile_bn();
@@ -196,6 +297,26 @@ int ea_attn_fwd(const ea_attn_args* args, void* stream) {
   const int cfg = choose_cfg(args);
   const ea::FwdParams p = make_params(args, cfg);
   e = ea::launch_fwd(p, args->in_dtype, (int)args->headdim, cfg, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    g_last_hip_error = (int)e;
+    return EA_EHIP;
+  }
+  return EA_OK;
+}
+
+int ea_attn_bwd(const ea_attn_bwd_args* args, void* stream) {
+  bool empty = false;
+  const int st = validate_bwd(args, &empty);
+  if (st != EA_OK || empty) return st;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    g_last_hip_error = (int)e;
+    return EA_EHIP;
+  }
+  if (!device_is_gfx950(dev)) return EA_EDEVICE;
+  const ea::BwdParams p = make_bwd_params(args);
+  e = ea::launch_bwd(p, args->dtype, (int)args->headdim, (hipStream_t)stream);
   if (e != hipSuccess) {
     g_last_hip_error = (int)e;
     return EA_EHIP;

@@ -1,0 +1,514 @@
+// Exact attention backward for gfx950: dQ, dK, dV by recomputing the
+// probabilities from Q, K and the forward's log-sum-exp.
+//
+// The pages obtain the backward pass by recomputation instead of storing the
+// N x N probabilities ("Flash Attention | Hermes Skill", Quick start: IO-aware
+// tiling and recomputation; FP8 section: the 16-bit kernels run forward and
+// backward).  With P_ij = exp(s_ij - LSE_i), the chain rule through the
+// standard-attention definition gives
+//     dV = P^T dO,  dP = dO V^T,  D_i = dO_i . O_i,  dS = P o (dP - D),
+//     dQ = scale dS K,  dK = scale dS^T Q.
+// Two kernels, no atomics (results do not depend on the order workgroups run
+// in):
+//   * attn_bwd_dq_kernel: one workgroup per (batch, head, 128 query rows),
+//     the mirror of the forward: Q^T and dO^T stay in registers (lane = query
+//     row), K and V tiles of 64 keys stream through LDS.  Per 32-key half:
+//     S^T = K Q^T and dP^T = V dO^T on the MFMA, dS^T = P^T o (dP^T - D) in
+//     the accumulator layout, which is the B-operand layout of
+//     dQ^T += K^T dS^T (K^T from the transposing LDS read).  It also computes
+//     D = rowsum(dO o O) and writes it for the second kernel.
+//   * attn_bwd_dkdv_kernel: one workgroup per (batch, K/V head, 128 keys), K^T
+//     and V^T in registers (lane = key), Q and dO tiles of 64 rows streaming
+//     through LDS, for every query head that reads this K/V head.  Per 32-row
+//     half: S = Q K^T, dP = dO V^T; P and dS in the accumulator layout (lane
+//     = key) are the B operands of dV^T += dO^T P and dK^T += Q^T dS, with
+//     dO^T and Q^T from the transposing LDS read.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "bwd_kernel.h"
+#include "kernel_common.h"
+
+namespace ea {
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <In IN, int D>
+struct BwdCfg {
+  static constexpr int kWaves = 4;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kRow = D * 2;                 // bytes per 16-bit row in LDS
+  static constexpr int kTile = 64 * kRow;            // a 64-row tile of K, V, Q or dO
+  static constexpr int kSteps = D / 16;              // MFMA k-steps over d
+  static constexpr int kDBlocks = D / 32;
+  static constexpr int kDma = kTile / 1024 / kWaves; // 1 KB DMA instructions per wave per tile
+};
+
+// Tile row and byte column of the 16-byte unit lane `ln` fetches in DMA block
+// `blk` of a 64-row tile (the swizzle of kernel_common.h applied in reverse).
+template <int ROW_BYTES>
+__device__ __forceinline__ uint32_t dma_offset(int blk, int ln, int row_stride) {
+  const int pos = blk * 64 + ln;
+  const int row = pos / (ROW_BYTES / 16);
+  const int phys = pos % (ROW_BYTES / 16);
+  return (uint32_t)(row * row_stride + swizzled_unit<ROW_BYTES>(row, phys) * 16);
+}
+
+// Byte range [base, base + bytes) of rows [r0, r0 + 64) of a head, cut at row
+// n (the buffer range makes rows past it read as zeros).
+struct Rows64 {
+  const unsigned char* base;
+  int bytes;
+};
+__device__ __forceinline__ Rows64 rows64(const unsigned char* head, int row_stride, int row_bytes, int r0, int n) {
+  const int rows = min(n - r0, 64);
+  return Rows64{head + (int64_t)r0 * row_stride, rows > 0 ? (rows - 1) * row_stride + row_bytes : 0};
+}
+
+// 32 lanes x 8 values of a 16-bit row fragment: lane holds d = 16 st + 8 half
+// + [0, 8) of row `row_ptr` for every k-step (zeros if !ok).
+template <int D>
+__device__ __forceinline__ void load_row_frags(uint4 (&f)[D / 16], const unsigned char* row_ptr, bool ok, int half) {
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st)
+    f[st] = ok ? *(const uint4*)(row_ptr + (16 * st + 8 * half) * 2) : make_uint4(0, 0, 0, 0);
+}
+
+template <In IN>
+__device__ __forceinline__ float dot8(uint4 a, uint4 b) {
+  const uint32_t wa[4] = {a.x, a.y, a.z, a.w};
+  const uint32_t wb[4] = {b.x, b.y, b.z, b.w};
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    s = __builtin_fmaf(unpack_lo<IN>(wa[i]), unpack_lo<IN>(wb[i]), s);
+    s = __builtin_fmaf(unpack_hi<IN>(wa[i]), unpack_hi<IN>(wb[i]), s);
+  }
+  return s;
+}
+
+// This lane's transposing-read offsets within a tile (see pv_half).
+template <int D>
+__device__ __forceinline__ void tr_offsets(uint32_t (&va)[2][D / 32], int lane) {
+  const int g = lane >> 4, sl = lane & 15;
+#pragma unroll
+  for (int r8 = 0; r8 < 2; ++r8)
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) {
+      const int vrow = 4 * (g >> 1) + (sl >> 2) + 8 * r8;
+      const int dcol = 32 * c + 16 * (g & 1) + 4 * (sl & 3);
+      va[r8][c] = (uint32_t)(lds_offset<D * 2>(vrow, dcol >> 3) + (dcol & 7) * 2);
+      asm volatile("" : "+v"(va[r8][c]));
+    }
+}
+
+// Row-read offsets of a tile: row `col` of a 32-row block, k-step st.
+template <int D>
+__device__ __forceinline__ void row_offsets(uint32_t (&ka)[D / 16], int col, int half) {
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st) {
+    ka[st] = (uint32_t)lds_offset<D * 2>(col, 2 * st + half);
+    asm volatile("" : "+v"(ka[st]));
+  }
+}
+
+// Write a 32-row x D accumulator held with lane = row (registers = columns
+// 32 c + 8 j + 4 half + [0, 4)) as 16-bit values times `mul`.
+template <In IN, int D>
+__device__ __forceinline__ void store_rows(unsigned char* row_ptr, const f32x16 (&acc)[D / 32], float mul, int half) {
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int d = 32 * c + 8 * j + 4 * half;
+      uint2 w;
+      w.x = pack2<IN>(acc[c][4 * j] * mul, acc[c][4 * j + 1] * mul);
+      w.y = pack2<IN>(acc[c][4 * j + 2] * mul, acc[c][4 * j + 3] * mul);
+      *(uint2*)(row_ptr + d * 2) = w;
+    }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// dQ (and D)
+// ---------------------------------------------------------------------------
+template <In IN, int D>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_bwd_dq_kernel(const BwdParams p) {
+  using C = BwdCfg<IN, D>;
+  __shared__ __attribute__((aligned(1024))) unsigned char kbuf0[C::kTile];
+  __shared__ __attribute__((aligned(1024))) unsigned char kbuf1[C::kTile];
+  __shared__ __attribute__((aligned(1024))) unsigned char vbuf0[C::kTile];
+  __shared__ __attribute__((aligned(1024))) unsigned char vbuf1[C::kTile];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int half = lane >> 5;
+  const int col = lane & 31;
+  const int n = p.n;
+
+  // heaviest query tiles first; groups of query heads sharing a K/V head on
+  // one XCD (workgroup w runs on XCD w % 8)
+  const int bh_count = p.batch * p.heads;
+  const int tile = p.q_tiles - 1 - (int)(blockIdx.x / bh_count);
+  int bh = (int)(blockIdx.x % bh_count);
+  if (p.group > 1 && bh_count % (8 * p.group) == 0) {
+    const int x = bh & 7, y = bh >> 3;
+    bh = ((y / p.group) * 8 + x) * p.group + y % p.group;
+  }
+  const int b = bh / p.heads;
+  const int h = bh - b * p.heads;
+  const int hkv = h / p.group;
+  const int q0 = tile * 128;
+  const int qrow = q0 + wave * 32 + col;
+  const bool ok = qrow < n;
+
+  // Q^T, dO^T in registers; D = dO . O (each lane holds half of the row's d)
+  uint4 qf[C::kSteps], df[C::kSteps];
+  float delta;
+  {
+    const int qr = ok ? qrow : 0;
+    load_row_frags<D>(qf, (const unsigned char*)p.q + ((int64_t)b * p.q_sb + (int64_t)h * p.q_sh + (int64_t)qr * p.q_ss) * 2, ok, half);
+    load_row_frags<D>(df, (const unsigned char*)p.dout + ((int64_t)b * p.do_sb + (int64_t)h * p.do_sh + (int64_t)qr * p.do_ss) * 2, ok, half);
+    uint4 of[C::kSteps];
+    load_row_frags<D>(of, (const unsigned char*)p.o + ((int64_t)b * p.o_sb + (int64_t)h * p.o_sh + (int64_t)qr * p.o_ss) * 2, ok, half);
+    float part = 0.f;
+#pragma unroll
+    for (int st = 0; st < C::kSteps; ++st) part += dot8<IN>(df[st], of[st]);
+    delta = part + __shfl_xor(part, 32);
+  }
+  // P = exp2(s c - lse log2 e); rows past n (and rows that saw no key) give 0
+  float lse2 = INFINITY;
+  if (ok) {
+    const float l = p.lse[(int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh + qrow];
+    if (__builtin_isfinite(l)) lse2 = l * kLog2e;
+  }
+  const float cexp = p.c_log2;
+
+  const KeyRange kr = tile_key_range(q0, 128, n, p.causal, p.wl, p.wr);
+  const int kt_begin = kr.lo / kBN;
+  const int kt_end = (kr.hi + kBN - 1) / kBN;
+  const int wr0 = q0 + wave * 32;
+  const int wr1 = min(wr0 + 32, n);
+  int vis_lo;
+  uint32_t vis_span;
+  {
+    vis_lo = p.wl >= 0 ? qrow - p.wl : 0;
+    int hi = n - 1;
+    if (p.causal) hi = min(hi, qrow);
+    if (p.wr >= 0) hi = min(hi, qrow + p.wr);
+    vis_span = (uint32_t)(hi - vis_lo);
+  }
+
+  const unsigned char* kg = (const unsigned char*)p.k + ((int64_t)b * p.k_sb + (int64_t)hkv * p.k_sh) * 2;
+  const unsigned char* vg = (const unsigned char*)p.v + ((int64_t)b * p.v_sb + (int64_t)hkv * p.v_sh) * 2;
+  const int k_stride = (int)(p.k_ss * 2), v_stride = (int)(p.v_ss * 2);
+  uint32_t k_off[C::kDma], v_off[C::kDma];
+#pragma unroll
+  for (int i = 0; i < C::kDma; ++i) {
+    k_off[i] = dma_offset<C::kRow>(wave * C::kDma + i, lane, k_stride);
+    v_off[i] = dma_offset<C::kRow>(wave * C::kDma + i, lane, v_stride);
+  }
+  auto issue = [&](int kt, unsigned char* kdst, unsigned char* vdst) {
+    const Rows64 rk = rows64(kg, k_stride, C::kRow, kt * kBN, n);
+    const Rows64 rv = rows64(vg, v_stride, C::kRow, kt * kBN, n);
+#pragma unroll
+    for (int i = 0; i < C::kDma; ++i) {
+      load_16b_to_lds(rk.base, rk.bytes, k_off[i], kdst + (wave * C::kDma + i) * 1024);
+      load_16b_to_lds(rv.base, rv.bytes, v_off[i], vdst + (wave * C::kDma + i) * 1024);
+    }
+  };
+  uint32_t ka[C::kSteps];
+  row_offsets<D>(ka, col, half);
+  uint32_t va[2][C::kDBlocks];
+  tr_offsets<D>(va, lane);
+
+  f32x16 acc[1][C::kDBlocks];
+#pragma unroll
+  for (int c = 0; c < C::kDBlocks; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[0][c][r] = 0.f;
+
+  // one 64-key tile from the slots (kc, vc)
+  auto step = [&](int kt, const unsigned char* kc, const unsigned char* vc) {
+    const bool masked = !block_all_visible(wr0, wr1, kt * kBN, kt * kBN + kBN, n, p.causal, p.wl, p.wr);
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      f32x16 s, dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[r] = 0.f;
+        dp[r] = 0.f;
+      }
+      const unsigned char* kb = kc + 32 * hb * C::kRow;
+      const unsigned char* vb = vc + 32 * hb * C::kRow;
+#pragma unroll
+      for (int st = 0; st < C::kSteps; ++st) {
+        s = mfma_16bit<IN>(*(const uint4*)(kb + ka[st]), qf[st], s);
+        dp = mfma_16bit<IN>(*(const uint4*)(vb + ka[st]), df[st], dp);
+      }
+      if (masked) {
+        const int base = kt * kBN + 32 * hb + 4 * half - vis_lo;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const uint32_t rel = (uint32_t)(base + 8 * (r >> 2) + (r & 3));
+          if (rel > vis_span) s[r] = -INFINITY;
+        }
+      }
+      uint32_t pk[1][8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * r], cexp, -lse2));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * r + 1], cexp, -lse2));
+        pk[0][r] = pack2<IN>(p0 * (dp[2 * r] - delta), p1 * (dp[2 * r + 1] - delta));
+      }
+      pv_half<IN, D, 1>(acc, pk, kc, va, hb);   // dQ^T += K^T dS^T
+    }
+  };
+
+  if (kt_begin < kt_end) {
+    issue(kt_begin, kbuf0, vbuf0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    int kt = kt_begin;
+    for (; kt + 1 < kt_end; kt += 2) {
+      issue(kt + 1, kbuf1, vbuf1);
+      step(kt, kbuf0, vbuf0);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (kt + 2 < kt_end) issue(kt + 2, kbuf0, vbuf0);
+      step(kt + 1, kbuf1, vbuf1);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+    if (kt < kt_end) step(kt, kbuf0, vbuf0);
+  }
+
+  if (ok) {
+    unsigned char* dqg = (unsigned char*)p.dq + ((int64_t)b * p.dq_sb + (int64_t)h * p.dq_sh + (int64_t)qrow * p.dq_ss) * 2;
+    store_rows<IN, D>(dqg, acc[0], p.scale, half);
+    if (half == 0) p.delta[(int64_t)b * p.delta_sb + (int64_t)h * p.delta_sh + qrow] = delta;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV
+// ---------------------------------------------------------------------------
+template <In IN, int D>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+attn_bwd_dkdv_kernel(const BwdParams p) {
+  using C = BwdCfg<IN, D>;
+  __shared__ __attribute__((aligned(1024))) unsigned char qbuf0[C::kTile];
+  __shared__ __attribute__((aligned(1024))) unsigned char qbuf1[C::kTile];
+  __shared__ __attribute__((aligned(1024))) unsigned char obuf0[C::kTile];
+  __shared__ __attribute__((aligned(1024))) unsigned char obuf1[C::kTile];
+  __shared__ __attribute__((aligned(16))) float lbuf[2][64];   // lse * log2(e) per query row
+  __shared__ __attribute__((aligned(16))) float dbuf[2][64];   // D per query row
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int half = lane >> 5;
+  const int col = lane & 31;
+  const int n = p.n;
+
+  // key blocks near the start first: under a causal mask they see the most queries
+  const int bhk_count = p.batch * p.heads_kv;
+  const int kb = (int)(blockIdx.x / bhk_count);
+  const int bhk = (int)(blockIdx.x % bhk_count);
+  const int b = bhk / p.heads_kv;
+  const int hkv = bhk - b * p.heads_kv;
+  const int k0 = kb * 128;
+  const int key = k0 + wave * 32 + col;
+  const bool kok = key < n;
+
+  // K^T and V^T in registers (lane = key)
+  uint4 kf[C::kSteps], vf[C::kSteps];
+  {
+    const int kr = kok ? key : 0;
+    load_row_frags<D>(kf, (const unsigned char*)p.k + ((int64_t)b * p.k_sb + (int64_t)hkv * p.k_sh + (int64_t)kr * p.k_ss) * 2, kok, half);
+    load_row_frags<D>(vf, (const unsigned char*)p.v + ((int64_t)b * p.v_sb + (int64_t)hkv * p.v_sh + (int64_t)kr * p.v_ss) * 2, kok, half);
+  }
+  const float cexp = p.c_log2;
+
+  // queries that can see a key of this block: [qlo, qhi)
+  int qlo = 0, qhi = n;
+  if (p.causal) qlo = max(qlo, k0);
+  if (p.wr >= 0) qlo = max(qlo, k0 - p.wr);
+  if (p.wl >= 0) qhi = min(qhi, k0 + 128 + p.wl);
+  const int qt_begin = qlo / 64;
+  const int qt_end = qhi > qlo ? (qhi + 63) / 64 : qt_begin;
+  // queries that see this lane's key: [qv_lo, qv_lo + qv_span]
+  int qv_lo = 0, qv_hi = n - 1;
+  if (p.causal) qv_lo = max(qv_lo, key);
+  if (p.wr >= 0) qv_lo = max(qv_lo, key - p.wr);
+  if (p.wl >= 0) qv_hi = min(qv_hi, key + p.wl);
+  const uint32_t qv_span = (uint32_t)(qv_hi - qv_lo);   // (keys past n: never stored)
+  const int kw0 = k0 + wave * 32;
+  const int kw1 = min(kw0 + 32, n);
+
+  const int q_stride = (int)(p.q_ss * 2), o_stride = (int)(p.do_ss * 2);
+  uint32_t q_off[C::kDma], o_off[C::kDma];
+#pragma unroll
+  for (int i = 0; i < C::kDma; ++i) {
+    q_off[i] = dma_offset<C::kRow>(wave * C::kDma + i, lane, q_stride);
+    o_off[i] = dma_offset<C::kRow>(wave * C::kDma + i, lane, o_stride);
+  }
+  uint32_t ka[C::kSteps];
+  row_offsets<D>(ka, col, half);
+  uint32_t va[2][C::kDBlocks];
+  tr_offsets<D>(va, lane);
+
+  f32x16 dk[1][C::kDBlocks], dv[1][C::kDBlocks];
+#pragma unroll
+  for (int c = 0; c < C::kDBlocks; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      dk[0][c][r] = 0.f;
+      dv[0][c][r] = 0.f;
+    }
+
+  // work: (query head of the group, query tile) pairs
+  const int qtiles = qt_end - qt_begin;
+  const int items = qtiles * p.group;
+  float row_val = 0.f;   // lse or D of one query row, staged through a register
+  auto issue = [&](int it, unsigned char* qdst, unsigned char* odst) {
+    const int gi = it / qtiles;
+    const int qt = qt_begin + it - gi * qtiles;
+    const int h = hkv * p.group + gi;
+    const unsigned char* qg = (const unsigned char*)p.q + ((int64_t)b * p.q_sb + (int64_t)h * p.q_sh) * 2;
+    const unsigned char* og = (const unsigned char*)p.dout + ((int64_t)b * p.do_sb + (int64_t)h * p.do_sh) * 2;
+    const Rows64 rq = rows64(qg, q_stride, C::kRow, qt * 64, n);
+    const Rows64 ro = rows64(og, o_stride, C::kRow, qt * 64, n);
+#pragma unroll
+    for (int i = 0; i < C::kDma; ++i) {
+      load_16b_to_lds(rq.base, rq.bytes, q_off[i], qdst + (wave * C::kDma + i) * 1024);
+      load_16b_to_lds(ro.base, ro.bytes, o_off[i], odst + (wave * C::kDma + i) * 1024);
+    }
+    const int r = qt * 64 + (tid & 63);
+    if (tid < 64) {
+      row_val = r < n ? p.lse[(int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh + r] : INFINITY;
+    } else if (tid < 128) {
+      row_val = r < n ? p.delta[(int64_t)b * p.delta_sb + (int64_t)h * p.delta_sh + r] : 0.f;
+    }
+  };
+  auto commit = [&](int slot) {
+    if (tid < 64) lbuf[slot][tid] = __builtin_isfinite(row_val) ? row_val * kLog2e : INFINITY;
+    else if (tid < 128) dbuf[slot][tid - 64] = row_val;
+  };
+
+  auto step = [&](int it, int slot, const unsigned char* qc, const unsigned char* oc) {
+    const int gi = it / qtiles;
+    const int q0 = (qt_begin + it - gi * qtiles) * 64;
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh) {
+      const int r0 = q0 + 32 * qh;
+      const bool masked = !block_all_visible(r0, min(r0 + 32, n), kw0, kw1 > kw0 ? kw1 : kw0 + 1, n, p.causal, p.wl, p.wr);
+      f32x16 s, dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[r] = 0.f;
+        dp[r] = 0.f;
+      }
+      const unsigned char* qb = qc + 32 * qh * C::kRow;
+      const unsigned char* ob = oc + 32 * qh * C::kRow;
+#pragma unroll
+      for (int st = 0; st < C::kSteps; ++st) {
+        s = mfma_16bit<IN>(*(const uint4*)(qb + ka[st]), kf[st], s);    // S = Q K^T (lane = key)
+        dp = mfma_16bit<IN>(*(const uint4*)(ob + ka[st]), vf[st], dp);  // dP = dO V^T
+      }
+      // registers r hold query rows r0 + 8 (r / 4) + 4 half + r % 4
+      if (masked) {
+        const int base = r0 + 4 * half - qv_lo;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const uint32_t rel = (uint32_t)(base + 8 * (r >> 2) + (r & 3));
+          if (rel > qv_span) s[r] = -INFINITY;
+        }
+      }
+      uint32_t pp[1][8], dsp[1][8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float4 l4 = *(const float4*)&lbuf[slot][32 * qh + 8 * j + 4 * half];
+        const float4 d4 = *(const float4*)&dbuf[slot][32 * qh + 8 * j + 4 * half];
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+        const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
+        float pr[4], ds[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          pr[t] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * j + t], cexp, -lv[t]));
+          ds[t] = pr[t] * (dp[4 * j + t] - dd[t]);
+        }
+        pp[0][2 * j] = pack2<IN>(pr[0], pr[1]);
+        pp[0][2 * j + 1] = pack2<IN>(pr[2], pr[3]);
+        dsp[0][2 * j] = pack2<IN>(ds[0], ds[1]);
+        dsp[0][2 * j + 1] = pack2<IN>(ds[2], ds[3]);
+      }
+      pv_half<IN, D, 1>(dv, pp, oc, va, qh);    // dV^T += dO^T P
+      pv_half<IN, D, 1>(dk, dsp, qc, va, qh);   // dK^T += Q^T dS
+    }
+  };
+
+  if (items > 0) {
+    issue(0, qbuf0, obuf0);
+    __builtin_amdgcn_s_waitcnt(0);
+    commit(0);
+    __syncthreads();
+    int it = 0;
+    for (; it + 1 < items; it += 2) {
+      issue(it + 1, qbuf1, obuf1);
+      step(it, 0, qbuf0, obuf0);
+      __builtin_amdgcn_s_waitcnt(0);
+      commit(1);
+      __syncthreads();
+      if (it + 2 < items) issue(it + 2, qbuf0, obuf0);
+      step(it + 1, 1, qbuf1, obuf1);
+      __builtin_amdgcn_s_waitcnt(0);
+      commit(0);
+      __syncthreads();
+    }
+    if (it < items) step(it, 0, qbuf0, obuf0);
+  }
+
+  if (kok) {
+    unsigned char* dkg = (unsigned char*)p.dk + ((int64_t)b * p.dk_sb + (int64_t)hkv * p.dk_sh + (int64_t)key * p.dk_ss) * 2;
+    unsigned char* dvg = (unsigned char*)p.dv + ((int64_t)b * p.dv_sb + (int64_t)hkv * p.dv_sh + (int64_t)key * p.dv_ss) * 2;
+    store_rows<IN, D>(dkg, dk[0], p.scale, half);
+    store_rows<IN, D>(dvg, dv[0], 1.f, half);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host-side launch
+// ---------------------------------------------------------------------------
+template <In IN, int D>
+static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
+  const dim3 block(256);
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<IN, D>), dim3((unsigned)((int64_t)p.q_tiles * p.batch * p.heads)), block, 0,
+                     stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<IN, D>), dim3((unsigned)((int64_t)p.k_blocks * p.batch * p.heads_kv)),
+                     block, 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd(const BwdParams& p, int in_dtype, int d, hipStream_t stream) {
+  if (in_dtype == 1 && d == 64) return launch_bwd_t<In::F16, 64>(p, stream);
+  if (in_dtype == 1 && d == 128) return launch_bwd_t<In::F16, 128>(p, stream);
+  if (in_dtype == 2 && d == 64) return launch_bwd_t<In::BF16, 64>(p, stream);
+  if (in_dtype == 2 && d == 128) return launch_bwd_t<In::BF16, 128>(p, stream);
+  return hipErrorInvalidValue;
+}
+
+const char* bwd_kernel_names(int in_dtype, int d) {
+  static const char* names[2][2] = {{"attn_bwd<f16,d64>", "attn_bwd<f16,d128>"}, {"attn_bwd<bf16,d64>", "attn_bwd<bf16,d128>"}};
+  if (in_dtype < 1 || in_dtype > 2 || (d != 64 && d != 128)) return "none";
+  return names[in_dtype - 1][d == 128];
+}
+
+}  // namespace ea

@@ -35,7 +35,7 @@
 extern "C" {
 #endif
 
-#define EA_ABI_VERSION 1u
+#define EA_ABI_VERSION 2u
 
 /* Status codes. */
 enum ea_status {
@@ -145,6 +145,75 @@ int ea_attn_fwd(const ea_attn_args* args, void* stream);
  * without a GPU.  info->struct_size must be set by the caller.
  */
 int ea_attn_plan(const ea_attn_args* args, ea_attn_plan_info* info);
+
+/*
+ * Arguments of one backward call: the gradients of a loss with respect to
+ * q, k and v given its gradient dout with respect to the forward's output o.
+ * The pages obtain them by recomputation ("Flash Attention | Hermes Skill",
+ * Quick start: IO-aware tiling and recomputation; its FP8 section: the 16-bit
+ * kernels run forward and backward, fp8 forward only).  With s the scaled,
+ * masked scores and P_ij = exp(s_ij - lse_i), the chain rule through the
+ * forward's definition gives
+ *     dv = P^T dout,   dP = dout v^T,   delta_i = dout_i . o_i,
+ *     dS = P o (dP - delta),   dq = scale dS k,   dk = scale dS^T q,
+ * with a shared K/V head's gradients summed over the query heads that read it.
+ * struct_size must be sizeof(ea_attn_bwd_args).
+ */
+typedef struct ea_attn_bwd_args {
+  uint32_t struct_size;
+  int32_t dtype;             /* EA_F16 or EA_BF16: q, k, v, o, dout, dq, dk, dv */
+  int32_t causal;            /* mask, as in ea_attn_args */
+  int32_t window_left;
+  int32_t window_right;
+  float softmax_scale;       /* finite and > 0, the forward's scale */
+  int64_t batch;             /* B >= 0 */
+  int64_t seqlen;            /* N >= 0 (queries and keys) */
+  int64_t nheads_q;          /* Hq >= 1 */
+  int64_t nheads_k;          /* Hk >= 1, Hq a multiple of Hk (shared K/V heads) */
+  int64_t headdim;           /* D: 64 or 128 */
+  const void* q;             /* [B, N, Hq, D] via the strides below (read) */
+  const void* k;             /* [B, N, Hk, D] (read) */
+  const void* v;             /* [B, N, Hk, D] (read) */
+  const void* o;             /* [B, N, Hq, D] the forward's output (read) */
+  const void* dout;          /* [B, N, Hq, D] gradient with respect to o (read) */
+  const float* lse;          /* [B, Hq, N] the forward's log-sum-exp (read) */
+  float* delta;              /* [B, Hq, N] written: dout_i . o_i in float32 */
+  void* dq;                  /* [B, N, Hq, D] written in full */
+  void* dk;                  /* [B, N, Hk, D] written in full */
+  void* dv;                  /* [B, N, Hk, D] written in full */
+  int64_t q_stride_b, q_stride_s, q_stride_h;
+  int64_t k_stride_b, k_stride_s, k_stride_h;
+  int64_t v_stride_b, v_stride_s, v_stride_h;
+  int64_t o_stride_b, o_stride_s, o_stride_h;
+  int64_t do_stride_b, do_stride_s, do_stride_h;
+  int64_t dq_stride_b, dq_stride_s, dq_stride_h;
+  int64_t dk_stride_b, dk_stride_s, dk_stride_h;
+  int64_t dv_stride_b, dv_stride_s, dv_stride_h;
+  int64_t lse_stride_b, lse_stride_h;       /* rows contiguous along N */
+  int64_t delta_stride_b, delta_stride_h;   /* rows contiguous along N */
+} ea_attn_bwd_args;
+
+/*
+ * ea_attn_bwd -- launch the backward on `stream` (a hipStream_t; NULL is the
+ * default stream).  Asynchronous, no allocation: two kernels in stream order
+ * (dq and delta, then dk and dv).  Results do not depend on the order in which
+ * workgroups run (no atomics).  All pointers are device pointers owned by the
+ * caller.
+ *   EA_EINVAL        args NULL or struct_size too small; a NULL pointer; a
+ *                    negative size; Hq or Hk < 1; a bad dtype enum; a
+ *                    non-finite softmax_scale; window bounds < -1; an output
+ *                    (dq, dk, dv, delta) overlapping an input or another
+ *                    output.
+ *   EA_EUNSUPPORTED  fp8 or float32 dtype; headdim not 64 or 128; Hq not a
+ *                    multiple of Hk; softmax_scale <= 0; a negative stride; a
+ *                    16-bit tensor's base not 16-byte aligned or a stride
+ *                    whose byte size is not a multiple of 16; lse or delta not
+ *                    4-byte aligned; an index that would overflow 32 bits.
+ *   EA_EDEVICE       the current device is not gfx950.
+ *   EA_EHIP          a launch failed.
+ * B == 0 or N == 0 returns EA_OK without launching.
+ */
+int ea_attn_bwd(const ea_attn_bwd_args* args, void* stream);
 
 /* Human-readable text for a status code (static storage, never NULL). */
 const char* ea_status_string(int status);

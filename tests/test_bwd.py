@@ -1,0 +1,198 @@
+"""GPU parity of the backward kernels against the float64 gradient oracle.
+
+Tolerance, derived from where the kernels round (u = 2^-8 for bf16, 2^-11 for
+fp16, the unit roundoff of the 16-bit format):
+  * P is rounded to 16 bits before dV = P^T dO; sums run in fp32.
+  * D_i = dO_i . O_i is computed from the 16-bit O the forward stored:
+    |dD_i| <= u sum_d |dO_id O_id|.
+  * dS = P (dP - D) is rounded to 16 bits before dK = scale dS^T Q and
+    dQ = scale dS K, so with E_ij = P_ij u sum_d |dO_id O_id| + u |dS_ij|:
+        |d dV|  <= 2 u (P^T |dO|) + ulp(dV)
+        |d dK|  <= 2 scale (E^T |Q|) + ulp(dK)
+        |d dQ|  <= 2 scale (E |K|) + ulp(dQ)
+    (factor 2: margin for the fp32 exp, the fp32 sums and the rounding of
+    P's own error), plus 1e-6 absolute for fp32 accumulation.
+  * delta: |d delta_i| <= 1e-5 (1 + sum_d |dO_id O_id|) (fp32 sum of exact
+    products of 16-bit values).
+The bound is computed elementwise from the oracle's float64 P, dP, D.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_attention_04_amd import attention, attention_backward
+from exact_attention_04_amd.workloads import small_case, torch_dtype
+
+pytestmark = pytest.mark.gpu
+
+U = {"f16": 2.0 ** -11, "bf16": 2.0 ** -8}
+MASKS = {
+    "none": (False, (-1, -1)),
+    "causal": (True, (-1, -1)),
+    "w17_5": (False, (17, 5)),
+    "causal_w100": (True, (100, -1)),
+    "diag": (False, (0, 0)),
+}
+
+
+def ulp16(x, dtype):
+    ax = np.abs(x)
+    e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
+    if dtype == "bf16":
+        return np.ldexp(1.0, (np.maximum(e, -126) - 7).astype(np.int64))
+    return np.ldexp(1.0, (np.maximum(e, -14) - 10).astype(np.int64))
+
+
+def to_bhsd(x, layout):
+    return x if layout == "bhsd" else np.swapaxes(x, 1, 2)
+
+
+def bounds(qf, kf, vf, dof, o16f, scale, causal, window, layout, dtype):
+    """Elementwise error bounds for dq, dk, dv (input layout) and delta."""
+    u = U[dtype]
+    q, k, v, do, o = (to_bhsd(x, layout) for x in (qf, kf, vf, dof, o16f))
+    B, H, N, D = q.shape
+    Hk = k.shape[1]
+    bq = np.zeros_like(q)
+    bk = np.zeros_like(k)
+    bv = np.zeros_like(v)
+    bd = np.zeros((B, H, N))
+    vis = oracle.visible(np.arange(N)[:, None], np.arange(N)[None, :], N, causal, window[0], window[1])
+    for b in range(B):
+        for h in range(H):
+            g = oracle.kv_head_of(h, H, Hk)
+            p = oracle.attention_probs_head(q[b, h], k[b, g], scale, causal, window[0], window[1])
+            p = np.where(vis, p, 0.0)
+            dp = do[b, h] @ v[b, g].T
+            dsum = np.sum(np.abs(do[b, h] * o[b, h]), axis=1)
+            d_exact = np.sum(do[b, h] * (p @ v[b, g]), axis=1)
+            e = p * (u * dsum)[:, None] + u * np.abs(p * (dp - d_exact[:, None]))
+            bv[b, g] += 2 * u * (p.T @ np.abs(do[b, h]))
+            bk[b, g] += 2 * scale * (e.T @ np.abs(q[b, h]))
+            bq[b, h] = 2 * scale * (e @ np.abs(k[b, g]))
+            bd[b, h] = 1e-5 * (1 + dsum)
+    back = (lambda x: x) if layout == "bhsd" else (lambda x: np.swapaxes(x, 1, 2))
+    return back(bq) + 1e-6, back(bk) + 1e-6, back(bv) + 1e-6, bd
+
+
+def f64(t):
+    return t.to(torch.float64).cpu().numpy()
+
+
+def check_bwd(B, H, Hk, N, D, dtype, mask, layout, seed, use_gpu_forward=False):
+    causal, window = MASKS[mask]
+    inp = small_case(B, H, N, D, dtype, layout, seed, heads_kv=Hk)
+    td = torch_dtype(dtype)
+    rng = np.random.default_rng(seed + 1)
+    do = torch.from_numpy(rng.standard_normal(tuple(inp.q.shape)).astype(np.float32)).to(td)
+    qf, kf, vf, dof = (f64(t) for t in (inp.q, inp.k, inp.v, do))
+    scale = 1.0 / math.sqrt(D)
+    q, k, v, dog = (t.cuda() for t in (inp.q, inp.k, inp.v, do))
+    if use_gpu_forward:
+        o, lse = attention(q, k, v, causal=causal, window_size=window, layout=layout)
+    else:
+        o_ref, lse_ref = oracle.attention(qf, kf, vf, scale, causal, window, layout)
+        o = torch.from_numpy(o_ref).to(td).cuda()
+        lse = torch.from_numpy(lse_ref).to(torch.float32).cuda()
+    dq, dk, dv, delta = attention_backward(q, k, v, o, dog, lse, causal=causal, window_size=window, layout=layout)
+    torch.cuda.synchronize()
+    o16f = f64(o)
+    dq_r, dk_r, dv_r, _ = oracle.attention_backward(qf, kf, vf, dof, scale, causal, window, layout)
+    bq, bk, bv, bd = bounds(qf, kf, vf, dof, o16f, scale, causal, window, layout, dtype)
+    if use_gpu_forward:
+        # the forward's own O error enters D: |dD_i| <= sum_d |dO_id| |dO_i|, with
+        # |dO| bounded by the forward's tolerance (2e-3 + one output ulp)
+        o_exact, _ = oracle.attention(qf, kf, vf, scale, causal, window, layout)
+        tol_o = 2e-3 + ulp16(o_exact, dtype)
+        extra = np.sum(np.abs(dof) * tol_o, axis=-1)        # per query row, input layout [.., N, H] or [.., H, N]
+        bq, bk = widen_for_forward_error(qf, kf, dof, scale, causal, window, layout, extra, bq, bk)
+    res = {}
+    for name, got, ref, bnd in (("dq", dq, dq_r, bq), ("dk", dk, dk_r, bk), ("dv", dv, dv_r, bv)):
+        g = f64(got)
+        assert np.isfinite(g).all(), f"{name} not finite"
+        err = np.abs(g - ref)
+        lim = bnd + ulp16(ref, dtype)
+        worst = float((err - lim).max())
+        res[name] = (float(err.max()), float((err / lim).max()))
+        assert worst <= 0, f"{name}: error exceeds the bound by {worst:.3g} (max err {err.max():.3g}, ratio {res[name][1]:.3g})"
+    d_exact = np.sum(dof * o16f, axis=-1)
+    d_exact = d_exact if layout == "bhsd" else np.swapaxes(d_exact, 1, 2)
+    derr = np.abs(f64(delta) - d_exact)
+    assert (derr <= bd).all(), f"delta: max err {derr.max():.3g}"
+    return res
+
+
+def widen_for_forward_error(qf, kf, dof, scale, causal, window, layout, extra, bq, bk):
+    """Add the effect of the forward's O error on D to the dq and dk bounds."""
+    q, k = to_bhsd(qf, layout), to_bhsd(kf, layout)
+    ex = extra if layout == "bhsd" else np.swapaxes(extra, 1, 2)       # [B, H, N]
+    B, H, N, D = q.shape
+    Hk = k.shape[1]
+    bq = to_bhsd(bq, layout).copy()
+    bk = to_bhsd(bk, layout).copy()
+    for b in range(B):
+        for h in range(H):
+            g = oracle.kv_head_of(h, H, Hk)
+            p = oracle.attention_probs_head(q[b, h], k[b, g], scale, causal, window[0], window[1])
+            e = 2 * p * ex[b, h][:, None]
+            bq[b, h] += scale * (e @ np.abs(k[b, g]))
+            bk[b, g] += scale * (e.T @ np.abs(q[b, h]))
+    back = (lambda x: x) if layout == "bhsd" else (lambda x: np.swapaxes(x, 1, 2))
+    return back(bq), back(bk)
+
+
+@pytest.mark.parametrize("mask", list(MASKS))
+@pytest.mark.parametrize("n", [1, 63, 64, 65, 130, 333])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_bwd_small_sweep(dtype, d, n, mask):
+    seed = 3000 + 10 * n + d + 7 * list(MASKS).index(mask) + (0 if dtype == "f16" else 100000)
+    check_bwd(2, 3, 3, n, d, dtype, mask, "bshd", seed)
+
+
+@pytest.mark.parametrize("layout", ["bshd", "bhsd"])
+@pytest.mark.parametrize("heads,heads_kv", [(4, 2), (4, 1), (6, 3)])
+@pytest.mark.parametrize("mask", ["none", "causal", "w17_5"])
+def test_bwd_shared_kv_and_layouts(heads, heads_kv, mask, layout):
+    check_bwd(1, heads, heads_kv, 200, 128, "bf16", mask, layout, 4000 + heads * 10 + heads_kv)
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f16", 64)])
+@pytest.mark.parametrize("mask", ["causal", "none"])
+def test_bwd_after_gpu_forward(dtype, d, mask):
+    # the whole pipeline: our forward's O and LSE feed the backward
+    check_bwd(2, 4, 2, 300, d, dtype, mask, "bshd", 4500 + d, use_gpu_forward=True)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_bwd_long_sequence(dtype):
+    # one head pair at N=2048: several 128-key blocks and query tiles per workgroup
+    check_bwd(1, 2, 1, 2048, 128, dtype, "causal", "bshd", 4600)
+
+
+def test_bwd_deterministic():
+    g = torch.Generator(device="cuda").manual_seed(5)
+    q, k, v, do = (torch.randn((2, 1000, 8, 128), device="cuda", generator=g).to(torch.bfloat16) for _ in range(4))
+    o, lse = attention(q, k, v, causal=True)
+    r1 = attention_backward(q, k, v, o, do, lse, causal=True)
+    for _ in range(3):
+        r2 = attention_backward(q, k, v, o, do, lse, causal=True)
+        torch.cuda.synchronize()
+        for a, b in zip(r1, r2):
+            assert torch.equal(a, b)
+
+
+def test_bwd_empty_and_errors():
+    x = torch.empty(0, 16, 2, 64, dtype=torch.float16, device="cuda")
+    l = torch.empty(0, 2, 16, dtype=torch.float32, device="cuda")
+    dq, dk, dv, delta = attention_backward(x, x, x, x, x, l)
+    assert dq.shape == x.shape
+    q = torch.zeros(1, 8, 2, 64, dtype=torch.float16, device="cuda")
+    lse = torch.zeros(1, 2, 8, dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError):
+        attention_backward(q.float(), q.float(), q.float(), q.float(), q.float(), lse)
+    with pytest.raises(ValueError):   # k and v with different head counts
+        attention_backward(q, q[:, :, :1].expand(1, 8, 3, 64), q, q, q, lse)
