@@ -1,7 +1,11 @@
 #!/usr/bin/env python3
 """Benchmark of the exact-attention forward on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--pass fwd|bwd]
+
+``--pass bwd`` measures the backward instead (dQ, dK, dV after one forward;
+2.5x the forward's flop, the five products S, dP, dV, dK, dQ) with the float64
+gradient oracle as the CPU baseline.
 
 Prints ONE JSON line.  A step is one forward call over the whole workload
 (inputs already resident in HBM): ``value`` is the whole-job throughput in
@@ -121,6 +125,81 @@ def time_gpu(w, steps: int, warmup: int):
     }
 
 
+def time_gpu_bwd(w, steps: int, warmup: int):
+    """Time the backward (both kernels) after one forward for O and LSE."""
+    import torch
+    from exact_attention_04_amd import attention, attention_backward
+    from exact_attention_04_amd.workloads import make_inputs
+
+    inp = make_inputs(w)
+    dev = torch.device("cuda", 0)
+    q, k, v = (t.to(dev) for t in (inp.q, inp.k, inp.v))
+    g = torch.Generator(device=dev).manual_seed(w.seed + 7)
+    do = torch.randn(q.shape, device=dev, generator=g).to(q.dtype)
+    kw = dict(causal=w.causal, window_size=(w.window_left, w.window_right), softmax_scale=w.softmax_scale,
+              layout=w.layout)
+    o, lse = attention(q, k, v, **kw)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty_like(lse)
+    for _ in range(warmup):
+        attention_backward(q, k, v, o, do, lse, dq=dq, dk=dk, dv=dv, delta=delta, **kw)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        attention_backward(q, k, v, o, do, lse, dq=dq, dk=dk, dv=dv, delta=delta, **kw)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kern_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return {"ms_per_step": (t1 - t0) * 1e3 / steps, "kernel_ms_avg": float(np.mean(kern_ms)),
+            "kernel_ms_median": float(np.median(kern_ms)), "kernel_ms_min": float(np.min(kern_ms))}
+
+
+def cpu_baseline_bwd(w, target_s: float = 12.0, max_procs: int = 16):
+    """Time the float64 gradient oracle on whole heads of the workload."""
+    import torch
+    import oracle
+    from oracle.sdpa_fp64 import make_pool
+    from oracle.sdpa_bwd_fp64 import attention_backward_parallel
+    from exact_attention_04_amd.workloads import make_inputs
+
+    inp = make_inputs(w)
+    cores = max(1, min(len(os.sched_getaffinity(0)), max_procs))
+    rng = np.random.default_rng(w.seed + 7)
+
+    def head(b, h):
+        g = oracle.kv_head_of(h, w.heads, w.kv_heads)
+        out = []
+        for t, hh in zip((inp.q, inp.k, inp.v), (h, g, g)):
+            x = t[b, :, hh, :] if w.layout == "bshd" else t[b, hh, :, :]
+            out.append(x.float().numpy())
+        out.append(rng.standard_normal(out[0].shape))
+        return tuple(out)
+
+    order = [(b, h) for h in range(w.heads) for b in range(w.batch)]
+    pool = make_pool(cores)
+    try:
+        list(pool.map(abs, range(cores)))
+        done, elapsed = 0, 0.0
+        while done < len(order) and elapsed < target_s:
+            batch = [head(b, h) for (b, h) in order[done:done + cores]]
+            t0 = time.perf_counter()
+            attention_backward_parallel(batch, w.softmax_scale, w.causal, (w.window_left, w.window_right), pool)
+            elapsed += time.perf_counter() - t0
+            done += len(batch)
+    finally:
+        pool.shutdown()
+    flops = 2.5 * workload_flops(w) * done / (w.batch * w.heads)
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} of {w.batch * w.heads} (batch, head) pairs, all rows, float64 numpy gradients, "
+                      f"one process per core; {elapsed:.1f} s wall", "seconds": elapsed}
+
+
 def copy_calibration(nbytes: int = 1 << 30):
     """A plain device copy of known size, for scaling HBM byte counters."""
     import torch
@@ -185,6 +264,8 @@ def main(argv=None):
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
+                    help="fwd: the forward (the headline metric); bwd: the backward (dQ, dK, dV)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (for HBM counter scaling)")
     args = ap.parse_args(argv)
@@ -198,6 +279,8 @@ def main(argv=None):
     from exact_attention_04_amd.workloads import HEADLINE, WORKLOADS
     name = args.workload or HEADLINE
     w = WORKLOADS[name]
+    if args.which == "bwd":
+        return main_bwd(args, name, w)
     flops = workload_flops(w)
 
     g = time_gpu(w, args.steps, args.warmup)
@@ -243,6 +326,39 @@ def main(argv=None):
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, target_s=args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+def main_bwd(args, name, w):
+    """One JSON line for the backward pass on workload `w` (16-bit inputs)."""
+    flops = 2.5 * workload_flops(w)   # five products of the forward's size: S, dP, dV, dK, dQ
+    g = time_gpu_bwd(w, args.steps, args.warmup)
+    achieved = flops / (g["kernel_ms_avg"] * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    esz = 2
+    q_el = w.batch * w.heads * w.seqlen * w.headdim
+    kv_el = w.batch * w.kv_heads * w.seqlen * w.headdim
+    nbytes = float(esz * (3 * q_el + 2 * kv_el) + esz * (q_el + 2 * kv_el) + 8 * w.batch * w.heads * w.seqlen)
+    rec = {
+        "metric": "attention bwd TFLOP/s (dQ, dK, dV; 2.5x the forward's flop)",
+        "value": round(flops / (g["ms_per_step"] * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(g["ms_per_step"], 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": name, "pass": "bwd", "batch": w.batch, "heads": w.heads, "kv_heads": w.kv_heads,
+                   "seqlen": w.seqlen, "headdim": w.headdim, "causal": w.causal,
+                   "window": [w.window_left, w.window_right], "layout": w.layout, "softmax_scale": w.softmax_scale},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": None,
+                     "kernel": "attn_bwd_dq + attn_bwd_dkdv", "kernel_ms_avg": round(g["kernel_ms_avg"], 5),
+                     "kernel_ms_median": round(g["kernel_ms_median"], 5), "flop_per_launch": flops,
+                     "algorithmic_bytes_per_launch": nbytes,
+                     "algorithmic_GBps": round(nbytes / (g["kernel_ms_avg"] * 1e-3) / 1e9, 1)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline_bwd(w, target_s=args.cpu_seconds)
     print(json.dumps(rec), flush=True)
     return 0
 

@@ -34,7 +34,7 @@ import numpy as np
 
 from .sdpa_fp64 import _key_span, _row_blocks, _softmax_block, _to_bhsd, kv_head_of, visible
 
-__all__ = ["attention_backward_head", "attention_backward"]
+__all__ = ["attention_backward_head", "attention_backward", "attention_backward_parallel"]
 
 
 def attention_backward_head(q, k, v, do, scale: float, causal: bool = False, window_left: int = -1,
@@ -101,3 +101,14 @@ def attention_backward(q, k, v, do, scale: Optional[float] = None, causal: bool 
     if layout == "bshd":
         dq, dk, dv = (np.swapaxes(x, 1, 2) for x in (dq, dk, dv))
     return dq, dk, dv, delta
+
+
+def _pool_task(args):
+    q, k, v, do, scale, causal, wl, wr = args
+    return attention_backward_head(q, k, v, do, scale, causal, wl, wr)
+
+
+def attention_backward_parallel(head_arrays, scale: float, causal: bool, window: Tuple[int, int], pool):
+    """``attention_backward_head`` over a list of (q, k, v, dO) heads on a ready process pool."""
+    tasks = [(q, k, v, do, scale, causal, int(window[0]), int(window[1])) for (q, k, v, do) in head_arrays]
+    return list(pool.map(_pool_task, tasks))
