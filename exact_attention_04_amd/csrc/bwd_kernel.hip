@@ -401,56 +401,131 @@ attn_bwd_dkdv_kernel(const BwdParams p) {
     else if (tid < 128) dbuf[slot][tid - 64] = row_val;
   };
 
+  // One 64-row tile (two halves a, b of 32 query rows) in four phases, so
+  // that the vector work of each half runs beside matrix work of the other:
+  //   1. S_a = Q_a K^T, dP_a = dO_a V^T
+  //   2. S_b, dP_b, step by step between the exp / dS / packing of half a
+  //   3. dV^T += dO_a^T P_a, dK^T += Q_a^T dS_a, between half b's vector work
+  //   4. dV^T += dO_b^T P_b, dK^T += Q_b^T dS_b
+  // (one wave per SIMD: nothing else hides the vector work).  Each step is
+  // fenced so the compiler keeps this order.
+  constexpr int kPV = 2 * C::kDBlocks;                 // P.V-like MFMAs per half and product
+  constexpr int kElemPerStep = 16 / C::kSteps;         // vector elements of a half per S step
+  constexpr int kElemPerPV = 16 / kPV;                 // ... per dV/dK MFMA pair
+  // registers r of a half hold query rows 8 (r / 4) + 4 half + r % 4
+  auto mask_half = [&](f32x16& s, int r0) {
+    const int base = r0 + 4 * half - qv_lo;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const uint32_t rel = (uint32_t)(base + 8 * (r >> 2) + (r & 3));
+      if (rel > qv_span) s[r] = -INFINITY;
+    }
+  };
+  auto row_vals = [&](int slot, int qh, float (&lv)[16], float (&dd)[16]) {
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const float4 l4 = *(const float4*)&lbuf[slot][32 * qh + 8 * jj + 4 * half];
+      const float4 d4 = *(const float4*)&dbuf[slot][32 * qh + 8 * jj + 4 * half];
+      lv[4 * jj] = l4.x; lv[4 * jj + 1] = l4.y; lv[4 * jj + 2] = l4.z; lv[4 * jj + 3] = l4.w;
+      dd[4 * jj] = d4.x; dd[4 * jj + 1] = d4.y; dd[4 * jj + 2] = d4.z; dd[4 * jj + 3] = d4.w;
+    }
+  };
+  // elements [e0, e0 + cnt) of a half: P, dS and their 16-bit pairs
+  auto vec_elems = [&](const f32x16& s, const f32x16& dp, const float (&lv)[16], const float (&dd)[16], int e0,
+                       int cnt, uint32_t (&pp)[8], uint32_t (&dsp)[8]) {
+#pragma unroll
+    for (int e = e0; e < e0 + cnt; e += 2) {
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], cexp, -lv[e]));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e + 1], cexp, -lv[e + 1]));
+      pp[e / 2] = pack2<IN>(p0, p1);
+      dsp[e / 2] = pack2<IN>(p0 * (dp[e] - dd[e]), p1 * (dp[e + 1] - dd[e + 1]));
+    }
+  };
+
+  // Operand reads run one phase ahead of the MFMAs that use them (LDS latency
+  // is otherwise paid on every product with one wave per SIMD).
+  auto row_frag = [&](const unsigned char* tile, int qh, int st) {
+    return *(const uint4*)(tile + 32 * qh * C::kRow + ka[st]);
+  };
+  auto tr_frag = [&](const unsigned char* tile, int qh, int m) {
+    const int jj = m / C::kDBlocks, c = m % C::kDBlocks;
+    const unsigned char* base = tile + (32 * qh + 16 * jj) * (2 * D);
+    const uint2 w0 = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + va[0][c])));
+    const uint2 w1 = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + va[1][c])));
+    return make_uint4(w0.x, w0.y, w1.x, w1.y);
+  };
+  auto pv_mfma = [&](f32x16 (&acc)[1][C::kDBlocks], uint4 a, const uint32_t (&pk)[8], int m) {
+    const int jj = m / C::kDBlocks, c = m % C::kDBlocks;
+    acc[0][c] = mfma_16bit<IN>(a, make_uint4(pk[4 * jj], pk[4 * jj + 1], pk[4 * jj + 2], pk[4 * jj + 3]), acc[0][c]);
+  };
+  static_assert(kPV == C::kSteps, "one dV/dK MFMA pair per S step");
+
   auto step = [&](int it, int slot, const unsigned char* qc, const unsigned char* oc) {
     const int gi = it / qtiles;
     const int q0 = (qt_begin + it - gi * qtiles) * 64;
+    const int kw1s = kw1 > kw0 ? kw1 : kw0 + 1;
+    const bool masked_a = !block_all_visible(q0, min(q0 + 32, n), kw0, kw1s, n, p.causal, p.wl, p.wr);
+    const bool masked_b = !block_all_visible(q0 + 32, min(q0 + 64, n), kw0, kw1s, n, p.causal, p.wl, p.wr);
+    f32x16 sa, dpa, sb, dpb;
 #pragma unroll
-    for (int qh = 0; qh < 2; ++qh) {
-      const int r0 = q0 + 32 * qh;
-      const bool masked = !block_all_visible(r0, min(r0 + 32, n), kw0, kw1 > kw0 ? kw1 : kw0 + 1, n, p.causal, p.wl, p.wr);
-      f32x16 s, dp;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[r] = 0.f;
-        dp[r] = 0.f;
-      }
-      const unsigned char* qb = qc + 32 * qh * C::kRow;
-      const unsigned char* ob = oc + 32 * qh * C::kRow;
-#pragma unroll
-      for (int st = 0; st < C::kSteps; ++st) {
-        s = mfma_16bit<IN>(*(const uint4*)(qb + ka[st]), kf[st], s);    // S = Q K^T (lane = key)
-        dp = mfma_16bit<IN>(*(const uint4*)(ob + ka[st]), vf[st], dp);  // dP = dO V^T
-      }
-      // registers r hold query rows r0 + 8 (r / 4) + 4 half + r % 4
-      if (masked) {
-        const int base = r0 + 4 * half - qv_lo;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const uint32_t rel = (uint32_t)(base + 8 * (r >> 2) + (r & 3));
-          if (rel > qv_span) s[r] = -INFINITY;
-        }
-      }
-      uint32_t pp[1][8], dsp[1][8];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float4 l4 = *(const float4*)&lbuf[slot][32 * qh + 8 * j + 4 * half];
-        const float4 d4 = *(const float4*)&dbuf[slot][32 * qh + 8 * j + 4 * half];
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-        const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
-        float pr[4], ds[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          pr[t] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * j + t], cexp, -lv[t]));
-          ds[t] = pr[t] * (dp[4 * j + t] - dd[t]);
-        }
-        pp[0][2 * j] = pack2<IN>(pr[0], pr[1]);
-        pp[0][2 * j + 1] = pack2<IN>(pr[2], pr[3]);
-        dsp[0][2 * j] = pack2<IN>(ds[0], ds[1]);
-        dsp[0][2 * j + 1] = pack2<IN>(ds[2], ds[3]);
-      }
-      pv_half<IN, D, 1>(dv, pp, oc, va, qh);    // dV^T += dO^T P
-      pv_half<IN, D, 1>(dk, dsp, qc, va, qh);   // dK^T += Q^T dS
+    for (int r = 0; r < 16; ++r) {
+      sa[r] = 0.f; dpa[r] = 0.f; sb[r] = 0.f; dpb[r] = 0.f;
     }
+    // 1: S_a, dP_a; half b's row fragments read meanwhile
+    uint4 qa[C::kSteps], oa[C::kSteps], qb[C::kSteps], ob[C::kSteps];
+#pragma unroll
+    for (int st = 0; st < C::kSteps; ++st) {
+      qa[st] = row_frag(qc, 0, st);
+      oa[st] = row_frag(oc, 0, st);
+    }
+    float lva[16], dda[16];
+    row_vals(slot, 0, lva, dda);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int st = 0; st < C::kSteps; ++st) {
+      sa = mfma_16bit<IN>(qa[st], kf[st], sa);      // S = Q K^T (lane = key)
+      dpa = mfma_16bit<IN>(oa[st], vf[st], dpa);    // dP = dO V^T
+      qb[st] = row_frag(qc, 1, st);
+      ob[st] = row_frag(oc, 1, st);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (masked_a) mask_half(sa, q0);
+    __builtin_amdgcn_sched_barrier(0);
+    // 2: S_b, dP_b beside half a's vector work; half a's transposed operands read meanwhile
+    uint32_t ppa[8], dsa[8];
+    uint4 tva[kPV], tka[kPV];
+#pragma unroll
+    for (int st = 0; st < C::kSteps; ++st) {
+      sb = mfma_16bit<IN>(qb[st], kf[st], sb);
+      dpb = mfma_16bit<IN>(ob[st], vf[st], dpb);
+      tva[st] = tr_frag(oc, 0, st);
+      tka[st] = tr_frag(qc, 0, st);
+      vec_elems(sa, dpa, lva, dda, st * kElemPerStep, kElemPerStep, ppa, dsa);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (masked_b) mask_half(sb, q0 + 32);
+    __builtin_amdgcn_sched_barrier(0);
+    // 3: dV^T += dO_a^T P_a, dK^T += Q_a^T dS_a beside half b's vector work
+    float lvb[16], ddb[16];
+    row_vals(slot, 1, lvb, ddb);
+    uint32_t ppb[8], dsb[8];
+    uint4 tvb[kPV], tkb[kPV];
+#pragma unroll
+    for (int m = 0; m < kPV; ++m) {
+      pv_mfma(dv, tva[m], ppa, m);
+      pv_mfma(dk, tka[m], dsa, m);
+      tvb[m] = tr_frag(oc, 1, m);
+      tkb[m] = tr_frag(qc, 1, m);
+      vec_elems(sb, dpb, lvb, ddb, m * kElemPerPV, kElemPerPV, ppb, dsb);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // 4
+#pragma unroll
+    for (int m = 0; m < kPV; ++m) {
+      pv_mfma(dv, tvb[m], ppb, m);
+      pv_mfma(dk, tkb[m], dsb, m);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   if (items > 0) {
