@@ -50,6 +50,8 @@ class AttnArgs(ctypes.Structure):
         ("v_stride_b", ctypes.c_int64), ("v_stride_s", ctypes.c_int64), ("v_stride_h", ctypes.c_int64),
         ("o_stride_b", ctypes.c_int64), ("o_stride_s", ctypes.c_int64), ("o_stride_h", ctypes.c_int64),
         ("lse_stride_b", ctypes.c_int64), ("lse_stride_h", ctypes.c_int64),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_int64),
     ]
 
 
@@ -89,6 +91,9 @@ class PlanInfo(ctypes.Structure):
         ("kv_tiles", ctypes.c_int64),
         ("masked_tiles", ctypes.c_int64),
         ("kernel", ctypes.c_char * 64),
+        ("workspace_bytes", ctypes.c_int64),
+        ("splits", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 

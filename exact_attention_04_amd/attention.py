@@ -73,6 +73,19 @@ def make_args(q, k, v, o, lse, *, causal=False, window_size=(-1, -1), softmax_sc
     return a
 
 
+# Workspace bytes wanted by the library, per argument signature (ea_attn_plan).
+_ws_bytes = {}
+
+
+def _workspace_bytes(a: _lib.AttnArgs) -> int:
+    key = bytes(a)[:_lib.AttnArgs.q.offset] + bytes(a)[_lib.AttnArgs.q_stride_b.offset:_lib.AttnArgs.workspace.offset]
+    n = _ws_bytes.get(key)
+    if n is None:
+        n = int(_lib.plan(a).workspace_bytes)
+        _ws_bytes[key] = n
+    return n
+
+
 def out_dtype_for(dtype: torch.dtype) -> torch.dtype:
     return torch.bfloat16 if dtype == torch.float8_e4m3fn else dtype
 
@@ -81,13 +94,16 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool
               window_size: Tuple[int, int] = (-1, -1), softmax_scale: Optional[float] = None,
               layout: str = "bshd", descale: Optional[Tuple[float, float, float]] = None,
               return_lse: bool = True, out: Optional[torch.Tensor] = None,
-              lse: Optional[torch.Tensor] = None):
+              lse: Optional[torch.Tensor] = None, split_kv: bool = True):
     """Exact attention forward on the current HIP stream.
 
     Returns ``(o, lse)``: o in q's layout and shape (bf16 for fp8 inputs, else
     q's dtype), lse as float32 [B, H, N] (None when ``return_lse`` is False).
     ``descale`` gives the per-tensor fp8 scales (stored value * descale = real
-    value).  Raises ValueError for arguments the library rejects.
+    value).  ``split_kv`` lets a launch with too few query tiles to fill the
+    GPU split each tile's keys into chunks (a scratch buffer from torch's
+    allocator, merged by a second kernel); False runs it unsplit.  Raises
+    ValueError for arguments the library rejects.
     """
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not t.is_cuda:
@@ -102,6 +118,12 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool
     a = make_args(q, k, v, out, lse, causal=causal, window_size=window_size, softmax_scale=softmax_scale,
                   layout=layout, descale=descale)
     stream = torch.cuda.current_stream(q.device).cuda_stream
+    ws = None
+    if split_kv and B > 0 and N > 0:
+        nbytes = _workspace_bytes(a)
+        if nbytes > 0:
+            ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+            a.workspace, a.workspace_bytes = ws.data_ptr(), nbytes
     _lib.check(_lib.fwd(a, stream))
     return out, lse
 

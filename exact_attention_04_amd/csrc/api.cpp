@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstddef>
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
@@ -60,9 +61,24 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 // Checks shared by ea_attn_fwd and ea_attn_plan.  Returns EA_OK, or the error.
 // Sets *empty when there is nothing to compute.
+// Version-1 sizes of the growing structs: everything before the fields added
+// since.
+constexpr size_t kArgsV1Size = offsetof(ea_attn_args, workspace);
+constexpr size_t kPlanV1Size = offsetof(ea_attn_plan_info, workspace_bytes);
+
+// The caller's workspace (pointer, bytes), or none when its struct predates it.
+void* workspace_of(const ea_attn_args* a, int64_t* bytes) {
+  if (a->struct_size < sizeof(ea_attn_args) || a->workspace == nullptr || a->workspace_bytes <= 0) {
+    *bytes = 0;
+    return nullptr;
+  }
+  *bytes = a->workspace_bytes;
+  return a->workspace;
+}
+
 int validate(const ea_attn_args* a, bool* empty) {
   *empty = false;
-  if (a == nullptr || a->struct_size < sizeof(ea_attn_args)) return EA_EINVAL;
+  if (a == nullptr || a->struct_size < kArgsV1Size) return EA_EINVAL;
   if (a->batch < 0 || a->seqlen_q < 0 || a->seqlen_k < 0 || a->nheads_q < 1 || a->nheads_k < 1 ||
       a->headdim < 1)
     return EA_EINVAL;
@@ -118,6 +134,16 @@ int validate(const ea_attn_args* a, bool* empty) {
   const Span sk = span_of(a->k, B, N, Hk, D, a->k_stride_b, a->k_stride_s, a->k_stride_h, ein);
   const Span sv = span_of(a->v, B, N, Hk, D, a->v_stride_b, a->v_stride_s, a->v_stride_h, ein);
   if (overlaps(so, sq) || overlaps(so, sk) || overlaps(so, sv)) return EA_EINVAL;
+  int64_t ws_bytes = 0;
+  if (void* ws = workspace_of(a, &ws_bytes)) {
+    if (!aligned16(ws)) return EA_EUNSUPPORTED;
+    const Span sw{(uintptr_t)ws, (uintptr_t)ws + (uintptr_t)ws_bytes};
+    if (overlaps(sw, so) || overlaps(sw, sq) || overlaps(sw, sk) || overlaps(sw, sv)) return EA_EINVAL;
+    if (a->lse != nullptr &&
+        overlaps(sw, Span{(uintptr_t)a->lse, (uintptr_t)a->lse + (uintptr_t)(((B - 1) * a->lse_stride_b +
+                                                                               (H - 1) * a->lse_stride_h + N) * 4)}))
+      return EA_EINVAL;
+  }
   return EA_OK;
 }
 
@@ -149,6 +175,9 @@ ea::FwdParams make_params(const ea_attn_args* a, int cfg) {
                    1.4426950408889634;
   p.c_log2 = (float)c;
   p.v_descale = fp8 ? a->v_descale : 1.0f;
+  p.splits = 1;
+  p.part_o = nullptr;
+  p.part_lse = nullptr;
   return p;
 }
 
@@ -252,6 +281,23 @@ ea::BwdParams make_bwd_params(const ea_attn_bwd_args* a) {
   return p;
 }
 
+// Key tiles of the query tile with the most (the kernel's visible key range).
+int max_kv_tiles(const ea::FwdParams& p, int cfg) {
+  const int bm = ea::tile_bm(cfg), bn = ea::tile_bn();
+  int best = 0;
+  for (int t = 0; t < p.q_tiles; ++t) {
+    const int q0 = t * bm;
+    const int qlast = std::min(q0 + bm, p.n) - 1;
+    const int lo = p.wl >= 0 ? std::max(0, q0 - p.wl) : 0;
+    int hi = p.n;
+    if (p.causal) hi = std::min(hi, qlast + 1);
+    if (p.wr >= 0) hi = std::min(hi, qlast + p.wr + 1);
+    hi = std::max(lo, hi);
+    best = std::max(best, (hi + bn - 1) / bn - lo / bn);
+  }
+  return best;
+}
+
 // Host-side mirror of the kernel's tile walk, for plan reports only.
 void count_tiles(const ea::FwdParams& p, int cfg, int64_t* tiles, int64_t* masked) {
   const int bm = ea::tile_bm(cfg), bn = ea::tile_bn();
@@ -279,6 +325,16 @@ void count_tiles(const ea::FwdParams& p, int cfg, int64_t* tiles, int64_t* maske
   *masked = t_mask * bh;
 }
 
+// Key chunks per query tile this call would use with a large enough workspace,
+// and the workspace that takes.
+int wanted_splits(const ea::FwdParams& p, int cfg, int d, int64_t* bytes) {
+  int64_t total = 0, masked = 0;
+  count_tiles(p, cfg, &total, &masked);
+  const int s = ea::choose_splits((int64_t)p.q_tiles * p.batch * p.heads, max_kv_tiles(p, cfg), total);
+  *bytes = ea::split_workspace_bytes(s, (int64_t)p.batch * p.heads, p.n, d);
+  return s;
+}
+
 }  // namespace
 
 extern "C" {
@@ -295,7 +351,15 @@ int ea_attn_fwd(const ea_attn_args* args, void* stream) {
   }
   if (!device_is_gfx950(dev)) return EA_EDEVICE;
   const int cfg = choose_cfg(args);
-  const ea::FwdParams p = make_params(args, cfg);
+  ea::FwdParams p = make_params(args, cfg);
+  int64_t need = 0, have = 0;
+  const int splits = wanted_splits(p, cfg, (int)args->headdim, &need);
+  void* ws = workspace_of(args, &have);
+  if (splits > 1 && ws != nullptr && have >= need) {
+    p.splits = splits;
+    p.part_o = (float*)ws;
+    p.part_lse = p.part_o + (int64_t)splits * p.batch * p.heads * p.n * args->headdim;
+  }
   e = ea::launch_fwd(p, args->in_dtype, (int)args->headdim, cfg, (hipStream_t)stream);
   if (e != hipSuccess) {
     g_last_hip_error = (int)e;
@@ -325,12 +389,13 @@ int ea_attn_bwd(const ea_attn_bwd_args* args, void* stream) {
 }
 
 int ea_attn_plan(const ea_attn_args* args, ea_attn_plan_info* info) {
-  if (info == nullptr || info->struct_size < sizeof(ea_attn_plan_info)) return EA_EINVAL;
+  if (info == nullptr || info->struct_size < kPlanV1Size) return EA_EINVAL;
   bool empty = false;
   const int st = validate(args, &empty);
   if (st != EA_OK) return st;
   const uint32_t sz = info->struct_size;
-  std::memset(info, 0, sizeof(ea_attn_plan_info));
+  const bool v2 = sz >= sizeof(ea_attn_plan_info);
+  std::memset(info, 0, v2 ? sizeof(ea_attn_plan_info) : kPlanV1Size);
   info->struct_size = sz;
   const int cfg = choose_cfg(args);
   info->block_m = ea::tile_bm(cfg);
@@ -342,6 +407,11 @@ int ea_attn_plan(const ea_attn_args* args, ea_attn_plan_info* info) {
   const ea::FwdParams p = make_params(args, cfg);
   info->grid = (int64_t)p.q_tiles * p.batch * p.heads;
   count_tiles(p, cfg, &info->kv_tiles, &info->masked_tiles);
+  if (v2) {
+    int64_t need = 0;
+    info->splits = wanted_splits(p, cfg, (int)args->headdim, &need);
+    info->workspace_bytes = need;
+  }
   return EA_OK;
 }
 

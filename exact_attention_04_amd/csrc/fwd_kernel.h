@@ -22,7 +22,20 @@ struct FwdParams {
   int causal, wl, wr;
   float c_log2;          // softmax_scale * q_descale * k_descale * log2(e)
   float v_descale;
+  // key chunks per query tile (1: no split); with more, the chunks' partial
+  // results go to part_o [splits][B H][N][D] and part_lse [splits][B H][N]
+  // (fp32) and a second kernel merges them
+  int splits;
+  float* part_o;
+  float* part_lse;
 };
+
+// Split of the keys for a launch of `items` query tiles x heads whose tiles
+// see at most `max_kv_tiles` key tiles and `total_kv_tiles` over all items:
+// 1 when the items already fill the GPU or their work is balanced.
+int choose_splits(int64_t items, int max_kv_tiles, int64_t total_kv_tiles);
+// Workspace bytes for `splits` chunks (0 for one).
+int64_t split_workspace_bytes(int splits, int64_t batch_heads, int64_t n, int d);
 
 // Tile configuration 0 (the only one): 128 query rows per workgroup (4 waves
 // of 32 rows, two waves per SIMD), 64 keys per K/V tile.

@@ -41,6 +41,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "fwd_kernel.h"
 #include "kernel_common.h"
 
@@ -96,9 +98,14 @@ attn_fwd_kernel(const FwdParams p) {
   // w % 8), so with K/V heads shared by groups of query heads the (batch,
   // head) order is permuted to put each whole group on one XCD, where its
   // K/V stays in that XCD's L2.
+  // With the keys split (p.splits > 1: too few query tiles to fill the GPU),
+  // workgroup item = (query tile, batch and head, key chunk), the chunk index
+  // varying fastest.
   const int bh_count = p.batch * p.heads;
-  const int tile = p.q_tiles - 1 - (int)(blockIdx.x / bh_count);
-  int bh = (int)(blockIdx.x % bh_count);
+  const int chunk = (int)(blockIdx.x % p.splits);
+  const int item = (int)(blockIdx.x / p.splits);
+  const int tile = p.q_tiles - 1 - item / bh_count;
+  int bh = item % bh_count;
   if (p.group > 1 && bh_count % (8 * p.group) == 0) {
     const int x = bh & 7, y = bh >> 3;
     bh = ((y / p.group) * 8 + x) * p.group + y % p.group;
@@ -116,8 +123,12 @@ attn_fwd_kernel(const FwdParams p) {
   const int v_row_stride = (int)(p.v_ss * C::kInBytes);
 
   const KeyRange kr = tile_key_range(q0, kBM, n, p.causal, p.wl, p.wr);
-  const int kt_begin = kr.lo / kBN;
-  const int kt_end = (kr.hi + kBN - 1) / kBN;
+  // this workgroup's key tiles: chunk `chunk` of p.splits contiguous chunks
+  // of the tile's visible key tiles (an empty chunk leaves l = 0)
+  const int kt_first = kr.lo / kBN;
+  const int kt_count = (kr.hi + kBN - 1) / kBN - kt_first;
+  const int kt_begin = kt_first + (int)((int64_t)kt_count * chunk / p.splits);
+  const int kt_end = kt_first + (int)((int64_t)kt_count * (chunk + 1) / p.splits);
 
   // ---- this wave's rows: RB blocks of 32, lane `col` owns one row in each
   const int wr0 = q0 + wave * 32 * RB;     // first row of the wave
@@ -641,7 +652,24 @@ attn_fwd_kernel(const FwdParams p) {
 #pragma unroll
   for (int qb = 0; qb < RB; ++qb) {
     const float l_row = l_part[qb] + __shfl_xor(l_part[qb], 32);
-    if (qrow[qb] < n) {
+    if (qrow[qb] < n && p.splits > 1) {
+      // partial result of this key chunk: normalised O in fp32 and its LSE,
+      // merged by attn_fwd_combine
+      const float inv = l_row > 0.f ? p.v_descale / l_row : 0.f;
+      const int64_t prow = ((int64_t)chunk * bh_count + bh) * n + qrow[qb];
+      float* po = p.part_o + prow * D;
+#pragma unroll
+      for (int c = 0; c < C::kDBlocks; ++c)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          *(float4*)(po + 32 * c + 8 * j + 4 * half) =
+              make_float4(acc[qb][c][4 * j] * inv, acc[qb][c][4 * j + 1] * inv, acc[qb][c][4 * j + 2] * inv,
+                          acc[qb][c][4 * j + 3] * inv);
+      if (half == 0)
+        p.part_lse[prow] = (m_run[qb] == -INFINITY || !(l_row > 0.f))
+                               ? -INFINITY
+                               : (m_run[qb] * cexp + __builtin_amdgcn_logf(l_row)) * kLn2;
+    } else if (qrow[qb] < n) {
       const float inv = l_row > 0.f ? p.v_descale / l_row : 0.f;
       constexpr int kOutBytes = 2;
       unsigned char* og = (unsigned char*)p.o +
@@ -669,17 +697,92 @@ attn_fwd_kernel(const FwdParams p) {
 // ---------------------------------------------------------------------------
 // Host-side launch
 // ---------------------------------------------------------------------------
+// Merge of the key chunks' partial results (p.splits > 1): per query row,
+// LSE = ln sum_s exp(LSE_s) and O = sum_s exp(LSE_s - LSE) O_s, written in
+// the output type; a row no chunk saw keeps O = 0, LSE = -inf.  One thread per
+// 4 columns of a row; HBM-bound.
+template <In OUT, int D>
+__global__ void __launch_bounds__(256) attn_fwd_combine(const FwdParams p) {
+  constexpr int kThreadsPerRow = D / 4;
+  constexpr int kRowsPerBlock = 256 / kThreadsPerRow;
+  const int64_t rows = (int64_t)p.batch * p.heads * p.n;
+  const int64_t r = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kThreadsPerRow;
+  if (r >= rows) return;
+  const int d = (threadIdx.x % kThreadsPerRow) * 4;
+  const int row = (int)(r % p.n);
+  const int bh = (int)(r / p.n);
+  const int b = bh / p.heads, h = bh - b * p.heads;
+  const int64_t stride = rows;   // between chunks
+  float m = -INFINITY;
+  for (int s = 0; s < p.splits; ++s) m = fmaxf(m, p.part_lse[s * stride + r]);
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  float lse = -INFINITY;
+  if (m != -INFINITY) {
+    float wsum = 0.f;
+    for (int s = 0; s < p.splits; ++s) {
+      const float w = __builtin_amdgcn_exp2f((p.part_lse[s * stride + r] - m) * 1.4426950408889634f);
+      if (w > 0.f) {
+        const float4 x = *(const float4*)(p.part_o + (s * stride + r) * D + d);
+        o.x = __builtin_fmaf(w, x.x, o.x);
+        o.y = __builtin_fmaf(w, x.y, o.y);
+        o.z = __builtin_fmaf(w, x.z, o.z);
+        o.w = __builtin_fmaf(w, x.w, o.w);
+      }
+      wsum += w;
+    }
+    const float inv = 1.f / wsum;
+    o = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+    lse = m + __builtin_amdgcn_logf(wsum) * kLn2;
+  }
+  unsigned char* og = (unsigned char*)p.o + ((int64_t)b * p.o_sb + (int64_t)h * p.o_sh + (int64_t)row * p.o_ss) * 2;
+  uint2 w;
+  w.x = pack2<OUT>(o.x, o.y);
+  w.y = pack2<OUT>(o.z, o.w);
+  *(uint2*)(og + d * 2) = w;
+  if (p.lse != nullptr && d == 0) p.lse[(int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh + row] = lse;
+}
+
 template <In IN, int D, int WAVES, int RB>
 static hipError_t launch_t(const FwdParams& p, hipStream_t stream) {
-  const dim3 grid((unsigned)((int64_t)p.q_tiles * p.batch * p.heads));
+  const dim3 grid((unsigned)((int64_t)p.q_tiles * p.batch * p.heads * p.splits));
   const dim3 block(64 * WAVES);
   hipLaunchKernelGGL((attn_fwd_kernel<IN, D, WAVES, RB>), grid, block, 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.splits == 1) return e;
+  constexpr In OUT = (IN == In::F16) ? In::F16 : In::BF16;
+  constexpr int kRowsPerBlock = 256 / (D / 4);
+  const int64_t rows = (int64_t)p.batch * p.heads * p.n;
+  hipLaunchKernelGGL((attn_fwd_combine<OUT, D>), dim3((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)),
+                     dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
 // One tile configuration: 128 query rows per workgroup (4 waves x 32 rows,
 // two workgroups per CU), 64 keys per K/V tile.
 int tile_bm(int /*cfg*/) { return 128; }
+
+// Key split.  Measured on gfx950: a split pays for its merge kernel (a few
+// microseconds) only where the query tiles' work is unbalanced (causal or
+// windowed masks), by cutting the heaviest tiles; on balanced launches it
+// costs.  So: no split when the items fill two workgroups per CU on the 256
+// CUs, or when the heaviest tile sees fewer than 1.5x the average key tiles;
+// otherwise enough chunks to bring the heaviest tile to about the average,
+// within the GPU's two-per-CU capacity, with at least two key tiles per chunk
+// and at most 16 chunks.
+int choose_splits(int64_t items, int max_kv_tiles, int64_t total_kv_tiles) {
+  constexpr int64_t kResident = 2 * 256;
+  if (items <= 0 || items >= kResident || total_kv_tiles <= 0) return 1;
+  if (2 * (int64_t)max_kv_tiles * items < 3 * total_kv_tiles) return 1;   // balanced
+  int64_t s = ((int64_t)max_kv_tiles * items + total_kv_tiles - 1) / total_kv_tiles;
+  s = std::min<int64_t>(s, (kResident + items - 1) / items);
+  s = std::min<int64_t>(s, max_kv_tiles / 2);
+  s = std::min<int64_t>(s, 16);
+  return (int)std::max<int64_t>(s, 1);
+}
+
+int64_t split_workspace_bytes(int splits, int64_t batch_heads, int64_t n, int d) {
+  return splits > 1 ? (int64_t)splits * batch_heads * n * (d + 1) * 4 : 0;
+}
 int tile_waves(int /*cfg*/) { return 4; }
 int tile_bn() { return kBN; }
 

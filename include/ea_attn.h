@@ -57,8 +57,10 @@ enum ea_dtype {
 };
 
 /*
- * Arguments of one forward call.  struct_size must be sizeof(ea_attn_args)
- * (the struct may grow at its end in later ABI versions).
+ * Arguments of one forward call.  struct_size is sizeof(ea_attn_args); the
+ * size of the version-1 struct (everything before `workspace`) is also
+ * accepted and means workspace == NULL.  The struct may grow at its end in
+ * later ABI versions.
  */
 typedef struct ea_attn_args {
   uint32_t struct_size;
@@ -96,11 +98,22 @@ typedef struct ea_attn_args {
   int64_t v_stride_b, v_stride_s, v_stride_h;
   int64_t o_stride_b, o_stride_s, o_stride_h;
   int64_t lse_stride_b, lse_stride_h;   /* LSE rows are contiguous along Nq */
+  /* Optional scratch for launches with too few query tiles to fill the GPU
+     (ea_attn_plan reports the bytes wanted, 0 if none): the keys of each tile
+     are then split into chunks whose partial results are merged by a second
+     kernel.  NULL, or fewer bytes than wanted, runs without the split (same
+     results up to rounding).  Device memory, 16-byte aligned, owned by the
+     caller; its contents need no initialisation and are overwritten; launches
+     that may run at the same time need separate workspaces. */
+  void* workspace;
+  int64_t workspace_bytes;
 } ea_attn_args;
 
 /* What ea_attn_fwd would launch for a given argument set. */
 typedef struct ea_attn_plan_info {
-  uint32_t struct_size;      /* set by the caller to sizeof(ea_attn_plan_info) */
+  uint32_t struct_size;      /* set by the caller to sizeof(ea_attn_plan_info); the
+                                version-1 size (up to `kernel`) is accepted and
+                                the fields after it are then not written */
   int32_t block_m;           /* query rows per workgroup */
   int32_t block_n;           /* keys per K/V tile */
   int32_t waves;             /* wavefronts per workgroup */
@@ -109,6 +122,9 @@ typedef struct ea_attn_plan_info {
   int64_t kv_tiles;          /* K/V tiles visited over the whole launch */
   int64_t masked_tiles;      /* of which need per-element masking */
   char kernel[64];           /* name of the kernel instantiation */
+  int64_t workspace_bytes;   /* ea_attn_args.workspace size that enables the key split */
+  int32_t splits;            /* key chunks per query tile with that workspace (1: none) */
+  int32_t reserved;
 } ea_attn_plan_info;
 
 /*

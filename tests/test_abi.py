@@ -54,8 +54,9 @@ def test_abi_version_and_status_strings():
 
 def test_struct_sizes_match_c():
     # same layout rules as the C compiler on x86-64 / amdgcn
-    assert ctypes.sizeof(_lib.AttnArgs) == 4 + 5 * 4 + 4 * 4 + 6 * 8 + 5 * 8 + 14 * 8
-    assert ctypes.sizeof(_lib.PlanInfo) == 4 + 4 * 4 + 4 + 3 * 8 + 64
+    assert ctypes.sizeof(_lib.AttnArgs) == 4 + 5 * 4 + 4 * 4 + 6 * 8 + 5 * 8 + 14 * 8 + 2 * 8
+    assert ctypes.sizeof(_lib.PlanInfo) == 4 + 4 * 4 + 4 + 3 * 8 + 64 + 8 + 2 * 4
+    assert ctypes.sizeof(_lib.BwdArgs) == 4 + 4 * 4 + 4 + 5 * 8 + 10 * 8 + 24 * 8 + 4 * 8
 
 
 def make(B=2, N=300, H=3, D=128, dtype=_lib.EA_BF16, layout="bshd", **kw):
@@ -82,6 +83,9 @@ def make(B=2, N=300, H=3, D=128, dtype=_lib.EA_BF16, layout="bshd", **kw):
     for k_, v_ in kw.items():
         setattr(a, k_, v_)
     return a
+
+
+SIZE = 2 * 300 * 3 * 128 * 4 + 4096   # make()'s spacing of the fake tensors
 
 
 def plan_status(a):
@@ -167,6 +171,48 @@ def test_shared_kv_heads():
         assert st == _lib.EA_OK, (hk, _lib.status_string(st))
         assert info.grid == 2 * 8 * math.ceil(300 / 128)
     assert plan_status(make(H=8, nheads_k=3))[0] == _lib.EA_EUNSUPPORTED
+
+
+def test_key_split_plan_and_workspace_rules():
+    # balanced work (no mask) is not split, however few the query tiles
+    st, info = plan_status(make(B=1, N=512, H=8, D=64, dtype=_lib.EA_F16))
+    assert st == 0 and info.splits == 1 and info.workspace_bytes == 0
+    # causal B2 H8 N2048: 256 items, the heaviest tile sees 32 key tiles
+    # against 17 on average -> 2 chunks
+    st, info = plan_status(make(B=2, N=2048, H=8, D=64, dtype=_lib.EA_F16, causal=1))
+    assert st == 0 and info.splits == 2
+    assert info.workspace_bytes == 2 * 16 * 2048 * (64 + 1) * 4
+    # causal B1 H2 N1000: 16 items -> up to 8 chunks, capped by the balance rule
+    st, info = plan_status(make(B=1, N=1000, H=2, D=128, causal=1))
+    assert st == 0 and info.splits == 2
+    # the headline shape fills the GPU: no split, no workspace
+    st, info = plan_status(make(B=4, N=4096, H=32, causal=1))
+    assert st == 0 and info.splits == 1 and info.workspace_bytes == 0
+    # a workspace must be 16-byte aligned and overlap no tensor
+    a = make(workspace=FAKE + 5 * SIZE + 8, workspace_bytes=4096)
+    assert plan_status(a)[0] == _lib.EA_EUNSUPPORTED
+    a = make(workspace=FAKE + 3 * SIZE, workspace_bytes=4096)           # inside o
+    assert plan_status(a)[0] == _lib.EA_EINVAL
+    a = make(workspace=FAKE + 4 * SIZE, workspace_bytes=4096)           # inside lse
+    assert plan_status(a)[0] == _lib.EA_EINVAL
+    assert plan_status(make(workspace=FAKE + 5 * SIZE, workspace_bytes=4096))[0] == _lib.EA_OK
+
+
+def test_version1_structs_are_accepted():
+    # callers built against the first ABI pass the structs without the
+    # workspace fields; the library then neither reads nor writes them
+    a = make(workspace=FAKE, workspace_bytes=64)   # would alias q if read
+    assert plan_status(a)[0] == _lib.EA_EINVAL
+    a.struct_size = _lib.AttnArgs.workspace.offset
+    assert plan_status(a)[0] == _lib.EA_OK
+    a.struct_size -= 8
+    assert plan_status(a)[0] == _lib.EA_EINVAL
+    info = _lib.PlanInfo()
+    info.struct_size = _lib.PlanInfo.workspace_bytes.offset
+    info.workspace_bytes = 12345
+    info.splits = 7
+    assert _lib.lib().ea_attn_plan(ctypes.byref(make(B=1, N=512, H=8, D=64, dtype=_lib.EA_F16)), ctypes.byref(info)) == 0
+    assert info.workspace_bytes == 12345 and info.splits == 7 and info.block_m == 128
 
 
 def test_fp8_argument_rules():

@@ -124,6 +124,28 @@ def test_shared_kv_workload_sampled(name):
     print(name, r)
 
 
+# ---------------------------------------------------------------------------
+# Key split for launches with few query tiles: both paths against the oracle
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("split", [True, False])
+@pytest.mark.parametrize("name", ["sdpa_b1h8n512d64_f16", "sdpa_b2h8n2048d64_f16", "sdpa_b2h8n2048d64_f16_causal"])
+def test_key_split_workloads(name, split):
+    w = WORKLOADS[name]
+    inp = make_inputs(w)
+    r = full_check(inp, w.dtype, causal=w.causal, window=(w.window_left, w.window_right), scale=w.softmax_scale,
+                   layout=w.layout, what=f"{name} split={split}", split_kv=split)
+    print(name, split, r)
+
+
+@pytest.mark.parametrize("mask", ["none", "causal", "w17_5", "causal_w100"])
+@pytest.mark.parametrize("n,d,dtype", [(1000, 128, "bf16"), (777, 64, "f16"), (1500, 128, "fp8")])
+def test_key_split_masks(n, d, dtype, mask):
+    causal, window = MASKS[mask]
+    inp = small_case(1, 2, n, d, dtype, "bshd", 7000 + n + d)
+    full_check(inp, dtype, causal=causal, window=window, what=f"split {dtype} n{n} {mask}", split_kv=True)
+
+
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("scale", [1.0, 2.0])
