@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libea_attn.so")
 
 EA_OK, EA_EINVAL, EA_EUNSUPPORTED, EA_EDEVICE, EA_EHIP = 0, 1, 2, 3, 4
 EA_F16, EA_BF16, EA_FP8_E4M3, EA_F32 = 1, 2, 3, 4
-EA_ABI_VERSION = 2
+EA_ABI_VERSION = 3
 
 # Every symbol the header declares.
 EXPORTS = ("ea_attn_fwd", "ea_attn_bwd", "ea_attn_plan", "ea_status_string", "ea_last_hip_error", "ea_abi_version")
@@ -52,6 +52,8 @@ class AttnArgs(ctypes.Structure):
         ("lse_stride_b", ctypes.c_int64), ("lse_stride_h", ctypes.c_int64),
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_int64),
+        ("pv_dtype", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 

@@ -42,7 +42,7 @@ def _dims(x: torch.Tensor, layout: str):
 
 
 def make_args(q, k, v, o, lse, *, causal=False, window_size=(-1, -1), softmax_scale=None,
-              layout="bshd", descale=None) -> _lib.AttnArgs:
+              layout="bshd", descale=None, pv_dtype=None) -> _lib.AttnArgs:
     """Fill an ``ea_attn_args`` for the given tensors (no checks beyond shapes)."""
     (B, N, H, D), (qb, qs, qh) = _dims(q, layout)
     (Bk, Nk, Hk, Dk), (kb, ks, kh) = _dims(k, layout)
@@ -70,6 +70,10 @@ def make_args(q, k, v, o, lse, *, causal=False, window_size=(-1, -1), softmax_sc
     if lse is not None:
         a.lse = lse.data_ptr()
         a.lse_stride_b, a.lse_stride_h = lse.stride(0), lse.stride(1)
+    if pv_dtype is not None:
+        if pv_dtype not in _DTYPES:
+            raise ValueError(f"unsupported pv_dtype {pv_dtype}")
+        a.pv_dtype = _DTYPES[pv_dtype]
     return a
 
 
@@ -94,7 +98,8 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool
               window_size: Tuple[int, int] = (-1, -1), softmax_scale: Optional[float] = None,
               layout: str = "bshd", descale: Optional[Tuple[float, float, float]] = None,
               return_lse: bool = True, out: Optional[torch.Tensor] = None,
-              lse: Optional[torch.Tensor] = None, split_kv: bool = True):
+              lse: Optional[torch.Tensor] = None, split_kv: bool = True,
+              pv_dtype: Optional[torch.dtype] = None):
     """Exact attention forward on the current HIP stream.
 
     Returns ``(o, lse)``: o in q's layout and shape (bf16 for fp8 inputs, else
@@ -102,8 +107,11 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool
     ``descale`` gives the per-tensor fp8 scales (stored value * descale = real
     value).  ``split_kv`` lets a launch with too few query tiles to fill the
     GPU split each tile's keys into chunks (a scratch buffer from torch's
-    allocator, merged by a second kernel); False runs it unsplit.  Raises
-    ValueError for arguments the library rejects.
+    allocator, merged by a second kernel); False runs it unsplit.
+    ``pv_dtype`` (fp8 inputs only): ``torch.float8_e4m3fn`` runs P.V with P
+    and V in e4m3 on the 8-bit matrix instructions; None or ``torch.bfloat16``
+    keeps P in bf16 (the default).  Raises ValueError for arguments the
+    library rejects.
     """
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not t.is_cuda:
@@ -116,7 +124,7 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool
     if not return_lse:
         lse = None
     a = make_args(q, k, v, out, lse, causal=causal, window_size=window_size, softmax_scale=softmax_scale,
-                  layout=layout, descale=descale)
+                  layout=layout, descale=descale, pv_dtype=pv_dtype)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     ws = None
     if split_kv and B > 0 and N > 0:

@@ -64,17 +64,21 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 // Version-1 sizes of the growing structs: everything before the fields added
 // since.
 constexpr size_t kArgsV1Size = offsetof(ea_attn_args, workspace);
+constexpr size_t kArgsV2Size = offsetof(ea_attn_args, pv_dtype);
 constexpr size_t kPlanV1Size = offsetof(ea_attn_plan_info, workspace_bytes);
 
 // The caller's workspace (pointer, bytes), or none when its struct predates it.
 void* workspace_of(const ea_attn_args* a, int64_t* bytes) {
-  if (a->struct_size < sizeof(ea_attn_args) || a->workspace == nullptr || a->workspace_bytes <= 0) {
+  if (a->struct_size < kArgsV2Size || a->workspace == nullptr || a->workspace_bytes <= 0) {
     *bytes = 0;
     return nullptr;
   }
   *bytes = a->workspace_bytes;
   return a->workspace;
 }
+
+// pv_dtype, or 0 when the caller's struct predates it.
+int32_t pv_dtype_of(const ea_attn_args* a) { return a->struct_size >= sizeof(ea_attn_args) ? a->pv_dtype : 0; }
 
 int validate(const ea_attn_args* a, bool* empty) {
   *empty = false;
@@ -91,9 +95,13 @@ int validate(const ea_attn_args* a, bool* empty) {
     if (!fp8 && d != 1.0f) return EA_EINVAL;
   }
   if (a->window_left < -1 || a->window_right < -1) return EA_EINVAL;
+  const int32_t pv = pv_dtype_of(a);
+  if (pv != 0 && pv != EA_BF16 && pv != EA_FP8_E4M3) return EA_EINVAL;
+  if (a->struct_size >= sizeof(ea_attn_args) && a->reserved != 0) return EA_EINVAL;
 
   // what the kernels implement
   if (a->in_dtype == EA_F32) return EA_EUNSUPPORTED;
+  if (!fp8 && pv != 0) return EA_EUNSUPPORTED;
   if (fp8 ? a->out_dtype != EA_BF16 : a->out_dtype != a->in_dtype) return EA_EUNSUPPORTED;
   if (a->headdim != 64 && a->headdim != 128) return EA_EUNSUPPORTED;
   if (fp8 && a->headdim != 128) return EA_EUNSUPPORTED;
@@ -147,8 +155,10 @@ int validate(const ea_attn_args* a, bool* empty) {
   return EA_OK;
 }
 
-// Tile configuration (see fwd_kernel.h): a single one for now.
-int choose_cfg(const ea_attn_args* /*a*/) { return 0; }
+// Kernel configuration (see fwd_kernel.h): 1 for e4m3 P.V, else 0.
+int choose_cfg(const ea_attn_args* a) {
+  return (a->in_dtype == EA_FP8_E4M3 && pv_dtype_of(a) == EA_FP8_E4M3) ? 1 : 0;
+}
 
 ea::FwdParams make_params(const ea_attn_args* a, int cfg) {
   ea::FwdParams p;
@@ -401,7 +411,7 @@ int ea_attn_plan(const ea_attn_args* args, ea_attn_plan_info* info) {
   info->block_m = ea::tile_bm(cfg);
   info->block_n = ea::tile_bn();
   info->waves = ea::tile_waves(cfg);
-  info->lds_bytes = ea::lds_bytes(args->in_dtype, (int)args->headdim);
+  info->lds_bytes = ea::lds_bytes(args->in_dtype, (int)args->headdim, cfg);
   std::strncpy(info->kernel, ea::kernel_name(args->in_dtype, (int)args->headdim, cfg), sizeof(info->kernel) - 1);
   if (empty) return EA_OK;
   const ea::FwdParams p = make_params(args, cfg);

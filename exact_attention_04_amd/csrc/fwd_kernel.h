@@ -37,12 +37,14 @@ int choose_splits(int64_t items, int max_kv_tiles, int64_t total_kv_tiles);
 // Workspace bytes for `splits` chunks (0 for one).
 int64_t split_workspace_bytes(int splits, int64_t batch_heads, int64_t n, int d);
 
-// Tile configuration 0 (the only one): 128 query rows per workgroup (4 waves
-// of 32 rows, two waves per SIMD), 64 keys per K/V tile.
+// Kernel configurations, both 128 query rows per workgroup (4 waves of 32
+// rows, two waves per SIMD) and 64 keys per K/V tile: 0, P.V in 16 bits
+// (fp8 V widened exactly to bf16); 1 (fp8 inputs only), P and V in e4m3 on
+// the 8-bit matrix instruction.
 int tile_bm(int cfg);
 int tile_waves(int cfg);
 int tile_bn();
-int lds_bytes(int in_dtype, int d);
+int lds_bytes(int in_dtype, int d, int cfg);
 const char* kernel_name(int in_dtype, int d, int cfg);
 hipError_t launch_fwd(const FwdParams& p, int in_dtype, int d, int cfg, hipStream_t stream);
 

@@ -48,29 +48,39 @@
 
 namespace ea {
 
-template <In IN, int D, int WAVES, int RB>
+template <In IN, int D, int WAVES, int RB, bool P8>
 struct Cfg {
   static constexpr bool kFp8 = (IN == In::FP8);
+  static_assert(!P8 || (kFp8 && D == 128), "e4m3 P.V: fp8 inputs, d = 128");
   static constexpr int kThreads = 64 * WAVES;
   static constexpr int kBM = 32 * RB * WAVES;        // query rows per workgroup
   static constexpr int kInBytes = kFp8 ? 1 : 2;
   static constexpr int kKRow = D * kInBytes;         // bytes per K row in LDS
-  static constexpr int kVRow = D * 2;                // V is 16-bit in LDS
+  static constexpr int kVRow = P8 ? D : D * 2;       // V in LDS: e4m3 for P8, else 16-bit
+  static constexpr bool kVWiden = kFp8 && !P8;       // fp8 V widened to bf16 through registers
   static constexpr int kKTile = kBN * kKRow;
   static constexpr int kVTile = kBN * kVRow;
   static constexpr int kStage = kKTile + kVTile;
-  // fp8 V: 16-byte global chunks per thread per tile (register staged)
+  // widened fp8 V: 16-byte global chunks per thread per tile (register staged)
   static constexpr int kVPer = kBN * D * kInBytes / 16 / kThreads;
-  static_assert(kFp8 ? (kBN * D * kInBytes / 16) % kThreads == 0 : true, "tile split");
+  static_assert(kVWiden ? (kBN * D * kInBytes / 16) % kThreads == 0 : true, "tile split");
   static_assert(kKTile % (1024 * WAVES) == 0 && kVTile % (1024 * WAVES) == 0, "DMA split");
   static constexpr int kQSteps = kFp8 ? D / 64 : D / 16;   // MFMA k-steps for S (per row block)
   static constexpr int kDBlocks = D / 32;                  // 32-wide output column blocks
 };
 
-template <In IN, int D, int WAVES, int RB>
+// LDS layout of an e4m3 V tile (64 rows of 128 bytes, 8 units of 16 bytes):
+// unit u of row r at unit u ^ v8_swz(r).  A transposing 8-bit read
+// (ds_read_b64_tr_b8) gathers, per 16-lane group, one unit of 8 rows
+// {b, b+1, b+2, b+3, b+8, ..., b+11} with b % 16 in {0, 4}; this swizzle puts
+// those 8 units at 8 distinct positions, so the read is free of bank
+// conflicts.
+__device__ __forceinline__ int v8_swz(int row) { return (row & 3) | (((row >> 3) & 1) << 2); }
+
+template <In IN, int D, int WAVES, int RB, bool P8>
 __global__ void __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(3 - RB, 3 - RB)))
 attn_fwd_kernel(const FwdParams p) {
-  using C = Cfg<IN, D, WAVES, RB>;
+  using C = Cfg<IN, D, WAVES, RB, P8>;
   constexpr In PIN = (IN == In::F16) ? In::F16 : In::BF16;   // type of P, V in LDS and O
   constexpr int kBM = C::kBM;
   // LDS: two K slots and two V slots.  K of tile i+1 and V of tile i are
@@ -170,9 +180,11 @@ attn_fwd_kernel(const FwdParams p) {
   // the last tile needs no special path and the slots need no clearing.  A
   // resource of range 0 (a tile past the visible range) makes the load write
   // zeros, into a slot that is then never read.
-  // fp8 V goes through registers and is widened to bf16 on the way into LDS.
+  // fp8 V for the bf16 P.V goes through registers and is widened to bf16 on
+  // the way into LDS; for the e4m3 P.V it goes straight in, in its own
+  // swizzle (v8_swz).
   constexpr int kKBlocks = C::kKTile / 1024 / WAVES;     // DMA instructions per wave, K
-  constexpr int kVBlocks = C::kFp8 ? 0 : C::kVTile / 1024 / WAVES;
+  constexpr int kVBlocks = C::kVWiden ? 0 : C::kVTile / 1024 / WAVES;
   constexpr int kVB = kVBlocks > 0 ? kVBlocks : 1;
   // Tile row and byte column of the unit lane `ln` fetches in DMA block `blk`.
   auto dma_row = [](int blk, int row_bytes, int ln) { return (blk * 64 + ln) / (row_bytes / 16); };
@@ -193,8 +205,14 @@ attn_fwd_kernel(const FwdParams p) {
 #pragma unroll
   for (int i = 0; i < kVB; ++i) {
     const int blk = wave * kVBlocks + i;
-    v_off[i] = kVBlocks > 0 ? (uint32_t)(dma_row(blk, C::kVRow, lane) * v_row_stride + dma_col(blk, C::kVRow, lane))
-                            : 0u;
+    if constexpr (P8) {
+      const int row = dma_row(blk, C::kVRow, lane);
+      const int phys = (blk * 64 + lane) % (C::kVRow / 16);
+      v_off[i] = (uint32_t)(row * v_row_stride + (phys ^ v8_swz(row)) * 16);
+    } else {
+      v_off[i] = kVBlocks > 0 ? (uint32_t)(dma_row(blk, C::kVRow, lane) * v_row_stride + dma_col(blk, C::kVRow, lane))
+                              : 0u;
+    }
   }
   // Buffer range of tile kt of a K or V head: the tile's first key and the
   // bytes up to the end of the sequence's last key (0 if kt >= kt_end).  The
@@ -209,15 +227,15 @@ attn_fwd_kernel(const FwdParams p) {
     const int rows = kt < kt_end ? min(n - k0, kBN) : 0;
     return TileRange{head + (int64_t)k0 * row_stride, rows > 0 ? (rows - 1) * row_stride + row_bytes : 0};
   };
-  uint4 vreg[C::kFp8 ? C::kVPer : 1];
+  uint4 vreg[C::kVWiden ? C::kVPer : 1];
   // One load of a tile: K block i, or V item i.
   constexpr int kDmaK = kKBlocks;
-  constexpr int kDmaV = C::kFp8 ? C::kVPer : kVBlocks;
+  constexpr int kDmaV = C::kVWiden ? C::kVPer : kVBlocks;
   auto load_k = [&](TileRange t, unsigned char* dst, int i) {
     load_16b_to_lds(t.base, t.bytes, k_off[i], dst + (wave * kKBlocks + i) * 1024);
   };
   auto load_v = [&](TileRange t, unsigned char* dst, int i) {
-    if constexpr (C::kFp8) {
+    if constexpr (C::kVWiden) {
       const int id = tid + i * C::kThreads;
       vreg[i] = load_16b(t.base, t.bytes, (uint32_t)((id / (D / 16)) * v_row_stride + (id % (D / 16)) * 16));
     } else {
@@ -236,9 +254,10 @@ attn_fwd_kernel(const FwdParams p) {
 #pragma unroll
     for (int i = 0; i < kDmaV; ++i) load_v(t, dst, i);
   };
-  // fp8 only: widen the V tile held in registers and store it (bf16) to LDS.
+  // widened fp8 V only: widen the V tile held in registers and store it
+  // (bf16) to LDS.
   auto store_v_fp8 = [&](unsigned char* vl) {
-    if constexpr (C::kFp8) {
+    if constexpr (C::kVWiden) {
 #pragma unroll
       for (int i = 0; i < C::kVPer; ++i) {
         const int id = tid + i * C::kThreads;
@@ -259,11 +278,15 @@ attn_fwd_kernel(const FwdParams p) {
     for (int c = 0; c < C::kDBlocks; ++c)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[qb][c][r] = 0.f;
+  // e4m3 P (P8) carries p * 2^kPShift: values up to 2^kPShift at the row
+  // reference stay clear of e4m3's top (448), values down to 2^-(6 + kPShift)
+  // stay normal.  O and l carry the same factor, so only the LSE removes it.
+  constexpr float kPShift = P8 ? 3.f : 0.f;
   float m_run[RB], neg_mc[RB], l_part[RB];
 #pragma unroll
   for (int qb = 0; qb < RB; ++qb) {
     m_run[qb] = -INFINITY;   // reference max of the raw (unscaled) scores
-    neg_mc[qb] = 0.f;        // -m_run * c, or 0 while no key was seen
+    neg_mc[qb] = 0.f;        // -m_run * c (+ kPShift), or 0 while no key was seen
     l_part[qb] = 0.f;        // this lane's share of the row sum
   }
   const float cexp = p.c_log2;                 // softmax scale * log2(e) (* fp8 descales)
@@ -282,7 +305,7 @@ attn_fwd_kernel(const FwdParams p) {
 
   // This lane's transposing-read offsets within a V tile (see pv_half).
   uint32_t va[2][C::kDBlocks];
-  {
+  if constexpr (!P8) {
     const int g = lane >> 4, sl = lane & 15;
 #pragma unroll
     for (int r8 = 0; r8 < 2; ++r8)
@@ -293,6 +316,23 @@ attn_fwd_kernel(const FwdParams p) {
         va[r8][c] = (uint32_t)(lds_offset<C::kVRow>(vrow, dcol >> 3) + (dcol & 7) * 2);
         asm volatile("" : "+v"(va[r8][c]));
       }
+  }
+  // e4m3 V (P8): this lane's offset, within a V tile, of its 8-bit
+  // transposing read for keys 8 (j/4) + 4 (g/2) + j%4, j = sl/2 (source lane
+  // sl of 16-lane group g reads 8 bytes of one such key row: columns
+  // 32 c + 16 (g%2) + 8 (sl%2) ..+7); the reads for keys 16 rr + those add
+  // 2048 rr bytes (16 rows; the swizzle depends on row bits 0, 1, 3 only).
+  uint32_t va8[P8 ? C::kDBlocks : 1];
+  if constexpr (P8) {
+    const int g = lane >> 4, sl = lane & 15;
+    const int j = sl >> 1;
+    const int row = 8 * (j >> 2) + 4 * (g >> 1) + (j & 3);
+#pragma unroll
+    for (int c = 0; c < C::kDBlocks; ++c) {
+      const int unit = 2 * c + (g & 1);
+      va8[c] = (uint32_t)(row * C::kVRow + ((unit ^ v8_swz(row)) << 4) + 8 * (sl & 1));
+      asm volatile("" : "+v"(va8[c]));
+    }
   }
 
   // This lane's K-fragment read offsets within a K tile, for k-step st of the
@@ -373,7 +413,7 @@ attn_fwd_kernel(const FwdParams p) {
       if (m_run[qb] == -INFINITY) {
         const float m = pair_max(fmaxf(block_max(sa[qb]), block_max(sb[qb])));
         m_run[qb] = m;
-        neg_mc[qb] = (m == -INFINITY) ? 0.f : -m * cexp;
+        neg_mc[qb] = (m == -INFINITY) ? 0.f : -m * cexp + kPShift;
       }
     }
   };
@@ -403,6 +443,73 @@ attn_fwd_kernel(const FwdParams p) {
         const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][2 * r + 1], cexp, neg_mc[qb]));
         pr[qb][r] = pack2<PIN>(e0 - unpack_lo<PIN>(pk[qb][r]), e1 - unpack_hi<PIN>(pk[qb][r]));
       }
+  };
+  // e4m3 P (P8): p * 2^kPShift for a 32-key half, rounded to nearest e4m3
+  // and packed four to a dword in accumulator order (byte t of dword w holds
+  // register 4 w + t); the row sum takes the unrounded fp32 values.  A value
+  // at or past 480 becomes NaN, which the epilogue's check turns into the
+  // exact-maximum pass.
+  auto exp_pack8 = [&](const f32x16 (&s)[RB], uint32_t (&pk)[RB][4]) {
+#pragma unroll
+    for (int qb = 0; qb < RB; ++qb)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        float e[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          e[t] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][4 * w + t], cexp, neg_mc[qb]));
+          l_part[qb] += e[t];
+        }
+        int x = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], 0, false);
+        x = __builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], x, true);
+        pk[qb][w] = (uint32_t)x;
+      }
+  };
+  // Its rounding residual times 16, p 2^(kPShift+4) - 16 e4m3(p 2^kPShift),
+  // itself rounded to e4m3 (the P.V of the residual takes the 2^-4 back
+  // through the matrix instruction's B scale): hi + lo / 16 carries p to
+  // about 2^-8 relative.
+  auto residual8 = [&](const f32x16 (&s)[RB], const uint32_t (&pk)[RB][4], uint32_t (&pr)[RB][4]) {
+#pragma unroll
+    for (int qb = 0; qb < RB; ++qb)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const f32x2 h01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)pk[qb][w], false);
+        const f32x2 h23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)pk[qb][w], true);
+        const float hi[4] = {h01[0], h01[1], h23[0], h23[1]};
+        float lo[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const float e16 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][4 * w + t], cexp, neg_mc[qb] + 4.f));
+          lo[t] = __builtin_fmaf(hi[t], -16.f, e16);
+        }
+        int x = __builtin_amdgcn_cvt_pk_fp8_f32(lo[0], lo[1], 0, false);
+        x = __builtin_amdgcn_cvt_pk_fp8_f32(lo[2], lo[3], x, true);
+        pr[qb][w] = (uint32_t)x;
+      }
+  };
+  // O^T += V^T P^T over a whole 64-key tile on the e4m3 matrix instruction
+  // (32x32x64).  P^T (B operand): lane l holds query l%32 and 32 keys, its 16
+  // of half a (bytes 0-15, `pa`) then its 16 of half b (`pb`), i.e. keys
+  // 32 (t/16) + 8 ((t%16)/4) + 4 (l/32) + t%4 for byte t.  The V^T fragment
+  // (A operand: row d = l%32 of a 32-column block, the same 32 keys) takes
+  // four transposing 8-bit reads (see va8), 8 keys each; each fragment feeds
+  // every row block.  `scale_b`: the B operand's power-of-two scale (E8M0,
+  // 127 = 1).
+  auto pv8 = [&](const uint32_t (&pa)[RB][4], const uint32_t (&pb)[RB][4], const unsigned char* vl, int scale_b) {
+#pragma unroll
+    for (int c = 0; c < C::kDBlocks; ++c) {
+      uint2 r[4];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+        r[rr] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vl + va8[c] + 2048 * rr)));
+      const uint4 a0 = make_uint4(r[0].x, r[0].y, r[1].x, r[1].y);
+      const uint4 a1 = make_uint4(r[2].x, r[2].y, r[3].x, r[3].y);
+#pragma unroll
+      for (int qb = 0; qb < RB; ++qb)
+        acc[qb][c] = mfma_fp8_scaled(a0, a1, make_uint4(pa[qb][0], pa[qb][1], pa[qb][2], pa[qb][3]),
+                                     make_uint4(pb[qb][0], pb[qb][1], pb[qb][2], pb[qb][3]), acc[qb][c], scale_b);
+    }
   };
   // S MFMAs of one half (K tile at `kn`) interleaved, step by step in program
   // order, with the softmax of the current half `sc`: step st issues the
@@ -522,6 +629,47 @@ attn_fwd_kernel(const FwdParams p) {
     pv_half<PIN, D, RB>(acc, pk, vl, va, hb);
     __builtin_amdgcn_sched_barrier(0);
   };
+  // e4m3 P.V (P8): a unit only computes the softmax of the current half
+  // (interleaved with the S MFMAs of the next tile's same half, as above) and
+  // packs P to e4m3; the P.V of the tile follows both halves (tile_pv8).
+  auto unit8 = [&](auto next_tag, f32x16 (&sc)[RB], int hb, const unsigned char* kn, f32x16 (&sn)[RB],
+                   uint32_t (&pk)[RB][4], auto&& hook) {
+    if constexpr (decltype(next_tag)::value) {
+      __builtin_amdgcn_s_setprio(1);
+      s_half(kn, hb, sn, hook);
+      exp_pack8(sc, pk);
+#pragma unroll
+      for (int i = 0; i < kSMfma; ++i) {
+        if (i % (4 * RB) == 0) __builtin_amdgcn_sched_group_barrier(0x100, 2 * C::kQSteps, 0);  // K reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                  // S MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, kExpValu / kSMfma, 0);                  // softmax VALU
+      }
+    } else {
+      exp_pack8(sc, pk);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // The tile's P.V from the e4m3 P of both halves.  e4m3 keeps 3 mantissa
+  // bits, so a tile whose rounding errors would not average out against the
+  // rest of a row -- one that adds more than 1/8 of some row's sum so far
+  // (the first tiles of every row, or a tile holding a row's dominant keys)
+  // -- also runs the P.V of the rounding residual (residual8), which brings
+  // P to about 2^-8 relative there.  `l_tile`: l_part before the tile.
+  auto tile_pv8 = [&](const f32x16 (&sa)[RB], const f32x16 (&sb)[RB], const uint32_t (&pa)[RB][4],
+                      const uint32_t (&pb)[RB][4], const float (&l_tile)[RB], const unsigned char* vl) {
+    __builtin_amdgcn_s_setprio(0);
+    bool heavy = false;
+#pragma unroll
+    for (int qb = 0; qb < RB; ++qb) heavy = heavy || ((l_part[qb] - l_tile[qb]) * 8.f > l_part[qb]);
+    if (__builtin_amdgcn_ballot_w64(heavy) != 0) {
+      uint32_t ra[RB][4], rb[RB][4];
+      residual8(sa, pa, ra);
+      residual8(sb, pb, rb);
+      pv8(ra, rb, vl, 127 - 4);
+    }
+    pv8(pa, pb, vl, 127);
+    __builtin_amdgcn_sched_barrier(0);
+  };
 
   // ---- the key loop.  Iteration i (tile kt = kt_begin + i) starts with the
   // scores S(i) in registers, K(i+1) and V(i) in LDS; it issues the DMA of
@@ -537,17 +685,30 @@ attn_fwd_kernel(const FwdParams p) {
     // previous iteration freed, spread over the S MFMAs of the first unit
     const TileRange rk = k_range(kt + 2), rv = v_range(kt + 1);
     constexpr int kPer = (kDmaK + kDmaV + C::kQSteps - 1) / C::kQSteps;
-    unit(BoolTag<true>{}, IntTag<kDmaK + kDmaV>{}, s_a, m_cur, 0, vread, kread, n_a, [&](int st) {
+    auto dma_hook = [&](int st) {
 #pragma unroll
       for (int u = 0; u < kPer; ++u) {
         const int i = st * kPer + u;
         if (i < kDmaK) load_k(rk, kwrite, i);
         else if (i < kDmaK + kDmaV) load_v(rv, vwrite, i - kDmaK);
       }
-    });
-    if (m_next) apply_mask(n_a, (kt + 1) * kBN, 0);
-    unit(BoolTag<true>{}, IntTag<0>{}, s_b, m_cur, 1, vread, kread, n_b, [](int) {});
-    if (m_next) apply_mask(n_b, (kt + 1) * kBN, 1);
+    };
+    if constexpr (P8) {
+      float l_tile[RB];
+#pragma unroll
+      for (int qb = 0; qb < RB; ++qb) l_tile[qb] = l_part[qb];
+      uint32_t pa[RB][4], pb[RB][4];
+      unit8(BoolTag<true>{}, s_a, 0, kread, n_a, pa, dma_hook);
+      if (m_next) apply_mask(n_a, (kt + 1) * kBN, 0);
+      unit8(BoolTag<true>{}, s_b, 1, kread, n_b, pb, [](int) {});
+      if (m_next) apply_mask(n_b, (kt + 1) * kBN, 1);
+      tile_pv8(s_a, s_b, pa, pb, l_tile, vread);
+    } else {
+      unit(BoolTag<true>{}, IntTag<kDmaK + kDmaV>{}, s_a, m_cur, 0, vread, kread, n_a, dma_hook);
+      if (m_next) apply_mask(n_a, (kt + 1) * kBN, 0);
+      unit(BoolTag<true>{}, IntTag<0>{}, s_b, m_cur, 1, vread, kread, n_b, [](int) {});
+      if (m_next) apply_mask(n_b, (kt + 1) * kBN, 1);
+    }
 #pragma unroll
     for (int qb = 0; qb < RB; ++qb) {
       s_a[qb] = n_a[qb];
@@ -589,8 +750,18 @@ attn_fwd_kernel(const FwdParams p) {
     // last tile: softmax and P.V only
     const unsigned char* vlast = odd ? vbuf1 : vbuf0;
     if (wave_needs_ref()) fold_max(s_a, s_b);
-    unit(BoolTag<false>{}, IntTag<0>{}, s_a, m_cur, 0, vlast, kbuf0, s_a, [](int) {});
-    unit(BoolTag<false>{}, IntTag<0>{}, s_b, m_cur, 1, vlast, kbuf0, s_b, [](int) {});
+    if constexpr (P8) {
+      float l_tile[RB];
+#pragma unroll
+      for (int qb = 0; qb < RB; ++qb) l_tile[qb] = l_part[qb];
+      uint32_t pa[RB][4], pb[RB][4];
+      unit8(BoolTag<false>{}, s_a, 0, kbuf0, s_a, pa, [](int) {});
+      unit8(BoolTag<false>{}, s_b, 1, kbuf0, s_b, pb, [](int) {});
+      tile_pv8(s_a, s_b, pa, pb, l_tile, vlast);
+    } else {
+      unit(BoolTag<false>{}, IntTag<0>{}, s_a, m_cur, 0, vlast, kbuf0, s_a, [](int) {});
+      unit(BoolTag<false>{}, IntTag<0>{}, s_b, m_cur, 1, vlast, kbuf0, s_b, [](int) {});
+    }
     __syncthreads();   // the slots are reused by a second pass
   };
   // Exact row maxima (second pass only): S and the mask, no softmax; one K
@@ -639,7 +810,7 @@ attn_fwd_kernel(const FwdParams p) {
     for (int qb = 0; qb < RB; ++qb) {
       const float m = pair_max(m_exact[qb]);
       m_run[qb] = m;
-      neg_mc[qb] = (m == -INFINITY) ? 0.f : -m * cexp;
+      neg_mc[qb] = (m == -INFINITY) ? 0.f : -m * cexp + kPShift;
       l_part[qb] = 0.f;
 #pragma unroll
       for (int c = 0; c < C::kDBlocks; ++c)
@@ -668,7 +839,7 @@ attn_fwd_kernel(const FwdParams p) {
       if (half == 0)
         p.part_lse[prow] = (m_run[qb] == -INFINITY || !(l_row > 0.f))
                                ? -INFINITY
-                               : (m_run[qb] * cexp + __builtin_amdgcn_logf(l_row)) * kLn2;
+                               : (m_run[qb] * cexp + __builtin_amdgcn_logf(l_row) - kPShift) * kLn2;
     } else if (qrow[qb] < n) {
       const float inv = l_row > 0.f ? p.v_descale / l_row : 0.f;
       constexpr int kOutBytes = 2;
@@ -687,7 +858,7 @@ attn_fwd_kernel(const FwdParams p) {
       if (p.lse != nullptr && half == 0) {
         const float lse = (m_run[qb] == -INFINITY || !(l_row > 0.f))
                               ? -INFINITY
-                              : (m_run[qb] * cexp + __builtin_amdgcn_logf(l_row)) * kLn2;
+                              : (m_run[qb] * cexp + __builtin_amdgcn_logf(l_row) - kPShift) * kLn2;
         p.lse[(int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh + qrow[qb]] = lse;
       }
     }
@@ -742,11 +913,11 @@ __global__ void __launch_bounds__(256) attn_fwd_combine(const FwdParams p) {
   if (p.lse != nullptr && d == 0) p.lse[(int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh + row] = lse;
 }
 
-template <In IN, int D, int WAVES, int RB>
+template <In IN, int D, int WAVES, int RB, bool P8 = false>
 static hipError_t launch_t(const FwdParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)((int64_t)p.q_tiles * p.batch * p.heads * p.splits));
   const dim3 block(64 * WAVES);
-  hipLaunchKernelGGL((attn_fwd_kernel<IN, D, WAVES, RB>), grid, block, 0, stream, p);
+  hipLaunchKernelGGL((attn_fwd_kernel<IN, D, WAVES, RB, P8>), grid, block, 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
   constexpr In OUT = (IN == In::F16) ? In::F16 : In::BF16;
@@ -757,8 +928,9 @@ static hipError_t launch_t(const FwdParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// One tile configuration: 128 query rows per workgroup (4 waves x 32 rows,
-// two workgroups per CU), 64 keys per K/V tile.
+// Kernel configurations: 128 query rows per workgroup (4 waves x 32 rows,
+// two workgroups per CU), 64 keys per K/V tile; configuration 1 (fp8 inputs
+// only) runs P.V on the e4m3 matrix instruction.
 int tile_bm(int /*cfg*/) { return 128; }
 
 // Key split.  Measured on gfx950: a split pays for its merge kernel (a few
@@ -786,14 +958,18 @@ int64_t split_workspace_bytes(int splits, int64_t batch_heads, int64_t n, int d)
 int tile_waves(int /*cfg*/) { return 4; }
 int tile_bn() { return kBN; }
 
-int lds_bytes(int in_dtype, int d) {
+int lds_bytes(int in_dtype, int d, int cfg) {
   const bool fp8 = in_dtype == 3;
   const int kin = fp8 ? 1 : 2;
-  return 2 * (kBN * d * kin + kBN * d * 2);
+  return 2 * (kBN * d * kin + kBN * d * (cfg == 1 ? 1 : 2));
 }
 
 hipError_t launch_fwd(const FwdParams& p, int in_dtype, int d, int cfg, hipStream_t stream) {
   // in_dtype: 1 = f16, 2 = bf16, 3 = fp8 e4m3 (validated by the caller)
+  if (cfg == 1) {
+    if (in_dtype == 3 && d == 128) return launch_t<In::FP8, 128, 4, 1, true>(p, stream);
+    return hipErrorInvalidValue;
+  }
   if (cfg != 0) return hipErrorInvalidValue;
   if (in_dtype == 1 && d == 64) return launch_t<In::F16, 64, 4, 1>(p, stream);
   if (in_dtype == 1 && d == 128) return launch_t<In::F16, 128, 4, 1>(p, stream);
@@ -803,10 +979,11 @@ hipError_t launch_fwd(const FwdParams& p, int in_dtype, int d, int cfg, hipStrea
   return hipErrorInvalidValue;
 }
 
-const char* kernel_name(int in_dtype, int d, int /*cfg*/) {
+const char* kernel_name(int in_dtype, int d, int cfg) {
   static const char* names[3][2] = {{"attn_fwd<f16,d64,bm128,bn64>", "attn_fwd<f16,d128,bm128,bn64>"},
                                     {"attn_fwd<bf16,d64,bm128,bn64>", "attn_fwd<bf16,d128,bm128,bn64>"},
                                     {"none", "attn_fwd<fp8,d128,bm128,bn64>"}};
+  if (cfg == 1) return (in_dtype == 3 && d == 128) ? "attn_fwd<fp8,pv8,d128,bm128,bn64>" : "none";
   if (in_dtype < 1 || in_dtype > 3 || (d != 64 && d != 128)) return "none";
   return names[in_dtype - 1][d == 128];
 }

@@ -17,6 +17,8 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
 constexpr int kBN = 64;            // keys per K/V tile
 constexpr float kLn2 = 0.6931471805599453f;
@@ -65,6 +67,13 @@ __device__ __forceinline__ f32x16 mfma_fp8(uint4 a0, uint4 a1, uint4 b0, uint4 b
   const i32x8 bv = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
   // formats 0/0: both operands OCP e4m3; scale exponents 127: no block scaling
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 0, 0, 0, 127, 0, 127);
+}
+
+// The same with B scaled by 2^(scale_b - 127) (E8M0 exponent).
+__device__ __forceinline__ f32x16 mfma_fp8_scaled(uint4 a0, uint4 a1, uint4 b0, uint4 b1, f32x16 c, int scale_b) {
+  const i32x8 av = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+  const i32x8 bv = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 0, 0, 0, 127, 0, scale_b);
 }
 
 // Pack two fp32 values into the P operand type (round to nearest even):

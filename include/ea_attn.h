@@ -35,7 +35,7 @@
 extern "C" {
 #endif
 
-#define EA_ABI_VERSION 2u
+#define EA_ABI_VERSION 3u
 
 /* Status codes. */
 enum ea_status {
@@ -58,9 +58,10 @@ enum ea_dtype {
 
 /*
  * Arguments of one forward call.  struct_size is sizeof(ea_attn_args); the
- * size of the version-1 struct (everything before `workspace`) is also
- * accepted and means workspace == NULL.  The struct may grow at its end in
- * later ABI versions.
+ * sizes of the version-1 struct (everything before `workspace`) and of the
+ * version-2 struct (everything before `pv_dtype`) are also accepted and mean
+ * workspace == NULL and pv_dtype == 0 as far as they lack them.  The struct
+ * may grow at its end in later ABI versions.
  */
 typedef struct ea_attn_args {
   uint32_t struct_size;
@@ -107,6 +108,16 @@ typedef struct ea_attn_args {
      that may run at the same time need separate workspaces. */
   void* workspace;
   int64_t workspace_bytes;
+  /* Number format of P and V in the P.V product, for fp8 inputs ("Flash
+     Attention | Hermes Skill", FP8 section: forward attention on e4m3
+     inputs; the pages leave the format of P open).  0 or EA_BF16: P rounded
+     to bf16 and V widened exactly to bf16, on the 16-bit matrix instructions
+     (the default).  EA_FP8_E4M3: P (times 2^3) rounded to e4m3 and V as
+     stored, on the 8-bit matrix instructions; a K/V tile that adds more than
+     1/8 of some query row's running sum also multiplies the e4m3 rounding
+     residual of P, so P keeps about 8 bits there.  For 16-bit inputs: 0. */
+  int32_t pv_dtype;
+  int32_t reserved;          /* 0 */
 } ea_attn_args;
 
 /* What ea_attn_fwd would launch for a given argument set. */
@@ -138,8 +149,10 @@ typedef struct ea_attn_plan_info {
  *                    negative size; Hq or Hk < 1; a bad dtype enum; a
  *                    non-finite softmax_scale; a descale that is not finite
  *                    and > 0, or != 1 for 16-bit inputs; window bounds < -1;
+ *                    pv_dtype not 0, EA_BF16 or EA_FP8_E4M3, or reserved != 0;
  *                    o overlapping q, k or v.
  *   EA_EUNSUPPORTED  float32 inputs; headdim not 64 or 128 (fp8: not 128);
+ *                    a nonzero pv_dtype with 16-bit inputs;
  *                    Nq != Nk; Hq not a multiple of Hk; softmax_scale <= 0; an output
  *                    dtype other than the one above; a negative stride; a
  *                    base pointer not 16-byte aligned or a b/s/h stride

@@ -45,11 +45,12 @@ def upload(inp: Inputs, device="cuda"):
     return tuple(t.to(device) for t in (inp.q, inp.k, inp.v))
 
 
-def run_gpu(inp: Inputs, *, causal=False, window=(-1, -1), scale=None, layout="bshd", split_kv=True):
+def run_gpu(inp: Inputs, *, causal=False, window=(-1, -1), scale=None, layout="bshd", split_kv=True,
+            pv_dtype=None):
     q, k, v = upload(inp)
     is_fp8 = inp.q.dtype == torch.float8_e4m3fn
     o, lse = attention(q, k, v, causal=causal, window_size=window, softmax_scale=scale, layout=layout,
-                       descale=inp.descale if is_fp8 else None, split_kv=split_kv)
+                       descale=inp.descale if is_fp8 else None, split_kv=split_kv, pv_dtype=pv_dtype)
     torch.cuda.synchronize()
     return o, lse
 
@@ -85,9 +86,10 @@ def kind_of(dtype: str) -> str:
 
 
 def full_check(inp: Inputs, dtype: str, *, causal=False, window=(-1, -1), scale=None, layout="bshd", what="",
-               split_kv=True):
+               split_kv=True, pv_dtype=None):
     """Whole-tensor comparison against the oracle (small shapes)."""
-    o, lse = run_gpu(inp, causal=causal, window=window, scale=scale, layout=layout, split_kv=split_kv)
+    o, lse = run_gpu(inp, causal=causal, window=window, scale=scale, layout=layout, split_kv=split_kv,
+                     pv_dtype=pv_dtype)
     qf, kf, vf = (stored_f64(t, s) for t, s in zip((inp.q, inp.k, inp.v), inp.descale))
     D = qf.shape[-1]
     sc = 1.0 / math.sqrt(D) if scale is None else scale

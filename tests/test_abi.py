@@ -54,7 +54,7 @@ def test_abi_version_and_status_strings():
 
 def test_struct_sizes_match_c():
     # same layout rules as the C compiler on x86-64 / amdgcn
-    assert ctypes.sizeof(_lib.AttnArgs) == 4 + 5 * 4 + 4 * 4 + 6 * 8 + 5 * 8 + 14 * 8 + 2 * 8
+    assert ctypes.sizeof(_lib.AttnArgs) == 4 + 5 * 4 + 4 * 4 + 6 * 8 + 5 * 8 + 14 * 8 + 2 * 8 + 2 * 4
     assert ctypes.sizeof(_lib.PlanInfo) == 4 + 4 * 4 + 4 + 3 * 8 + 64 + 8 + 2 * 4
     assert ctypes.sizeof(_lib.BwdArgs) == 4 + 4 * 4 + 4 + 5 * 8 + 10 * 8 + 24 * 8 + 4 * 8
 
@@ -213,6 +213,30 @@ def test_version1_structs_are_accepted():
     info.splits = 7
     assert _lib.lib().ea_attn_plan(ctypes.byref(make(B=1, N=512, H=8, D=64, dtype=_lib.EA_F16)), ctypes.byref(info)) == 0
     assert info.workspace_bytes == 12345 and info.splits == 7 and info.block_m == 128
+
+
+def test_version2_structs_are_accepted():
+    # callers built against the second ABI pass the struct without pv_dtype
+    a = make(dtype=_lib.EA_FP8_E4M3, pv_dtype=99, reserved=5)   # invalid if read
+    assert plan_status(a)[0] == _lib.EA_EINVAL
+    a.struct_size = _lib.AttnArgs.pv_dtype.offset
+    st, info = plan_status(a)
+    assert st == _lib.EA_OK and info.kernel.decode() == "attn_fwd<fp8,d128,bm128,bn64>"
+
+
+def test_pv_dtype_rules():
+    # fp8 inputs: 0 / bf16 keep P in bf16, e4m3 selects the 8-bit P.V kernel
+    for pv, name, lds in ((0, "attn_fwd<fp8,d128,bm128,bn64>", 2 * (8192 + 16384)),
+                          (_lib.EA_BF16, "attn_fwd<fp8,d128,bm128,bn64>", 2 * (8192 + 16384)),
+                          (_lib.EA_FP8_E4M3, "attn_fwd<fp8,pv8,d128,bm128,bn64>", 2 * (8192 + 8192))):
+        st, info = plan_status(make(dtype=_lib.EA_FP8_E4M3, pv_dtype=pv))
+        assert st == _lib.EA_OK and info.kernel.decode() == name and info.lds_bytes == lds
+    assert plan_status(make(dtype=_lib.EA_FP8_E4M3, pv_dtype=_lib.EA_F16))[0] == _lib.EA_EINVAL
+    assert plan_status(make(dtype=_lib.EA_FP8_E4M3, pv_dtype=_lib.EA_FP8_E4M3, reserved=1))[0] == _lib.EA_EINVAL
+    # 16-bit inputs take no pv_dtype
+    assert plan_status(make(pv_dtype=_lib.EA_FP8_E4M3))[0] == _lib.EA_EUNSUPPORTED
+    assert plan_status(make(pv_dtype=_lib.EA_BF16))[0] == _lib.EA_EUNSUPPORTED
+    assert _lib.lib().ea_attn_fwd(ctypes.byref(make(pv_dtype=_lib.EA_FP8_E4M3)), None) == _lib.EA_EUNSUPPORTED
 
 
 def test_fp8_argument_rules():
