@@ -2,8 +2,11 @@
 """Benchmark of the exact-attention forward on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--pass fwd|bwd]
+                    [--pv-dtype bf16|e4m3]
 
-``--pass bwd`` measures the backward instead (dQ, dK, dV after one forward;
+``--pv-dtype e4m3`` (fp8 workloads) times the P.V product in e4m3 on the
+8-bit matrix instructions instead of bf16.  ``--pass bwd`` measures the
+backward instead (dQ, dK, dV after one forward;
 2.5x the forward's flop, the five products S, dP, dV, dK, dQ) with the float64
 gradient oracle as the CPU baseline.
 
@@ -76,9 +79,9 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
+def measured_traffic(workload: str, pv8: bool = False):
     """HBM bytes per launch from a committed counter summary, if still current."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}{'_pv8' if pv8 else ''}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -88,7 +91,7 @@ def measured_traffic(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def time_gpu(w, steps: int, warmup: int):
+def time_gpu(w, steps: int, warmup: int, pv8: bool = False):
     import torch
     from exact_attention_04_amd import attention, plan
     from exact_attention_04_amd.workloads import make_inputs
@@ -100,6 +103,8 @@ def time_gpu(w, steps: int, warmup: int):
     lse = torch.empty((w.batch, w.heads, w.seqlen), dtype=torch.float32, device=dev)
     kw = dict(causal=w.causal, window_size=(w.window_left, w.window_right), softmax_scale=w.softmax_scale,
               layout=w.layout, descale=inp.descale if w.dtype == "fp8" else None)
+    if pv8:
+        kw["pv_dtype"] = torch.float8_e4m3fn
     info = plan(q, k, v, o, lse, **kw)
     for _ in range(warmup):
         attention(q, k, v, out=o, lse=lse, **kw)
@@ -266,6 +271,8 @@ def main(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
                     help="fwd: the forward (the headline metric); bwd: the backward (dQ, dK, dV)")
+    ap.add_argument("--pv-dtype", choices=("bf16", "e4m3"), default="bf16",
+                    help="fp8 workloads: number format of P and V in the P.V product")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (for HBM counter scaling)")
     args = ap.parse_args(argv)
@@ -281,15 +288,19 @@ def main(argv=None):
     w = WORKLOADS[name]
     if args.which == "bwd":
         return main_bwd(args, name, w)
+    pv8 = args.pv_dtype == "e4m3"
+    if pv8 and w.dtype != "fp8":
+        print("--pv-dtype e4m3 applies to fp8 workloads only", file=sys.stderr)
+        return 2
     flops = workload_flops(w)
 
-    g = time_gpu(w, args.steps, args.warmup)
+    g = time_gpu(w, args.steps, args.warmup, pv8)
     if args.copy_calibration:
         copy_calibration()
     value = flops / (g["ms_per_step"] * 1e-3) / 1e12
     achieved = flops / (g["kernel_ms_avg"] * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
-    traffic = measured_traffic(name)
+    traffic = measured_traffic(name, pv8)
     rec = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -307,6 +318,7 @@ def main(argv=None):
             "workload": name, "batch": w.batch, "heads": w.heads, "kv_heads": w.kv_heads, "seqlen": w.seqlen, "headdim": w.headdim,
             "causal": w.causal, "window": [w.window_left, w.window_right], "layout": w.layout,
             "softmax_scale": w.softmax_scale,
+            **({"pv_dtype": "e4m3"} if pv8 else {}),
         },
         "roofline": {
             "bound": "mfma",
