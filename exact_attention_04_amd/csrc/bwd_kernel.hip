@@ -298,19 +298,39 @@ attn_bwd_dq_kernel(const BwdParams p) {
 // ---------------------------------------------------------------------------
 // dK, dV
 // ---------------------------------------------------------------------------
+// One workgroup of 8 waves per (batch, K/V head, 128 keys), two roles per 32
+// keys (waves w and w + 4, which the hardware places on the same SIMD):
+//   * role A (waves 0-3): S = Q K^T, P = exp2(S c - lse log2 e), dV^T += dO^T P;
+//     P also goes to LDS;
+//   * role B (waves 4-7), one tile behind: dP = dO V^T, dS = P o (dP - D)
+//     with P from LDS, dK^T += Q^T dS.
+// Each role issues 32 MFMAs per 64-row tile, and the two waves of a SIMD
+// interleave one's vector work with the other's MFMAs.  Q and dO tiles of 64
+// rows stream through three LDS slots: role A reads tile i, role B tile i - 1,
+// and the DMA fills tile i + 1.  K^T (role A) or V^T (role B) and the dV^T or
+// dK^T accumulators stay in registers (lane = key).
 template <In IN, int D>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_bwd_dkdv_kernel(const BwdParams p) {
   using C = BwdCfg<IN, D>;
+  constexpr int kDma = C::kTile / 1024 / 8;   // 1 KB DMA instructions per wave per tile and tensor
+  // three slots as separate objects, so the compiler can tell the DMA into one
+  // from the reads of another (a single array would make it wait for the DMA)
   __shared__ __attribute__((aligned(1024))) unsigned char qbuf0[C::kTile];
   __shared__ __attribute__((aligned(1024))) unsigned char qbuf1[C::kTile];
+  __shared__ __attribute__((aligned(1024))) unsigned char qbuf2[C::kTile];
   __shared__ __attribute__((aligned(1024))) unsigned char obuf0[C::kTile];
   __shared__ __attribute__((aligned(1024))) unsigned char obuf1[C::kTile];
-  __shared__ __attribute__((aligned(16))) float lbuf[2][64];   // lse * log2(e) per query row
-  __shared__ __attribute__((aligned(16))) float dbuf[2][64];   // D per query row
+  __shared__ __attribute__((aligned(1024))) unsigned char obuf2[C::kTile];
+  // P of a tile from role A to role B: [parity][wave pair][16-byte group j][lane]
+  __shared__ __attribute__((aligned(1024))) uint4 pbuf[2][4][4][64];
+  __shared__ __attribute__((aligned(16))) float lbuf[3][64];   // lse * log2(e) per query row
+  __shared__ __attribute__((aligned(16))) float dbuf[3][64];   // D per query row
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool role_b = wave >= 4;
+  const int kw = wave & 3;           // which 32 keys of the block
   const int lane = tid & 63;
   const int half = lane >> 5;
   const int col = lane & 31;
@@ -323,15 +343,17 @@ attn_bwd_dkdv_kernel(const BwdParams p) {
   const int b = bhk / p.heads_kv;
   const int hkv = bhk - b * p.heads_kv;
   const int k0 = kb * 128;
-  const int key = k0 + wave * 32 + col;
+  const int key = k0 + kw * 32 + col;
   const bool kok = key < n;
 
-  // K^T and V^T in registers (lane = key)
-  uint4 kf[C::kSteps], vf[C::kSteps];
+  // K^T (role A) or V^T (role B) in registers (lane = key)
+  uint4 kvf[C::kSteps];
   {
     const int kr = kok ? key : 0;
-    load_row_frags<D>(kf, (const unsigned char*)p.k + ((int64_t)b * p.k_sb + (int64_t)hkv * p.k_sh + (int64_t)kr * p.k_ss) * 2, kok, half);
-    load_row_frags<D>(vf, (const unsigned char*)p.v + ((int64_t)b * p.v_sb + (int64_t)hkv * p.v_sh + (int64_t)kr * p.v_ss) * 2, kok, half);
+    const unsigned char* src = role_b
+        ? (const unsigned char*)p.v + ((int64_t)b * p.v_sb + (int64_t)hkv * p.v_sh + (int64_t)kr * p.v_ss) * 2
+        : (const unsigned char*)p.k + ((int64_t)b * p.k_sb + (int64_t)hkv * p.k_sh + (int64_t)kr * p.k_ss) * 2;
+    load_row_frags<D>(kvf, src, kok, half);
   }
   const float cexp = p.c_log2;
 
@@ -348,29 +370,21 @@ attn_bwd_dkdv_kernel(const BwdParams p) {
   if (p.wr >= 0) qv_lo = max(qv_lo, key - p.wr);
   if (p.wl >= 0) qv_hi = min(qv_hi, key + p.wl);
   const uint32_t qv_span = (uint32_t)(qv_hi - qv_lo);   // (keys past n: never stored)
-  const int kw0 = k0 + wave * 32;
+  const int kw0 = k0 + kw * 32;
   const int kw1 = min(kw0 + 32, n);
 
   const int q_stride = (int)(p.q_ss * 2), o_stride = (int)(p.do_ss * 2);
-  uint32_t q_off[C::kDma], o_off[C::kDma];
-#pragma unroll
-  for (int i = 0; i < C::kDma; ++i) {
-    q_off[i] = dma_offset<C::kRow>(wave * C::kDma + i, lane, q_stride);
-    o_off[i] = dma_offset<C::kRow>(wave * C::kDma + i, lane, o_stride);
-  }
   uint32_t ka[C::kSteps];
   row_offsets<D>(ka, col, half);
   uint32_t va[2][C::kDBlocks];
   tr_offsets<D>(va, lane);
 
-  f32x16 dk[1][C::kDBlocks], dv[1][C::kDBlocks];
+  // dV^T (role A) or dK^T (role B)
+  f32x16 acc[1][C::kDBlocks];
 #pragma unroll
   for (int c = 0; c < C::kDBlocks; ++c)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      dk[0][c][r] = 0.f;
-      dv[0][c][r] = 0.f;
-    }
+    for (int r = 0; r < 16; ++r) acc[0][c][r] = 0.f;
 
   // work: (query head of the group, query tile) pairs
   const int qtiles = qt_end - qt_begin;
@@ -385,9 +399,12 @@ attn_bwd_dkdv_kernel(const BwdParams p) {
     const Rows64 rq = rows64(qg, q_stride, C::kRow, qt * 64, n);
     const Rows64 ro = rows64(og, o_stride, C::kRow, qt * 64, n);
 #pragma unroll
-    for (int i = 0; i < C::kDma; ++i) {
-      load_16b_to_lds(rq.base, rq.bytes, q_off[i], qdst + (wave * C::kDma + i) * 1024);
-      load_16b_to_lds(ro.base, ro.bytes, o_off[i], odst + (wave * C::kDma + i) * 1024);
+    for (int i = 0; i < kDma; ++i) {
+      // (recomputed per tile: a few VALU instead of registers held across the loop)
+      load_16b_to_lds(rq.base, rq.bytes, dma_offset<C::kRow>(wave * kDma + i, lane, q_stride),
+                      qdst + (wave * kDma + i) * 1024);
+      load_16b_to_lds(ro.base, ro.bytes, dma_offset<C::kRow>(wave * kDma + i, lane, o_stride),
+                      odst + (wave * kDma + i) * 1024);
     }
     const int r = qt * 64 + (tid & 63);
     if (tid < 64) {
@@ -401,17 +418,10 @@ attn_bwd_dkdv_kernel(const BwdParams p) {
     else if (tid < 128) dbuf[slot][tid - 64] = row_val;
   };
 
-  // One 64-row tile (two halves a, b of 32 query rows) in four phases, so
-  // that the vector work of each half runs beside matrix work of the other:
-  //   1. S_a = Q_a K^T, dP_a = dO_a V^T
-  //   2. S_b, dP_b, step by step between the exp / dS / packing of half a
-  //   3. dV^T += dO_a^T P_a, dK^T += Q_a^T dS_a, between half b's vector work
-  //   4. dV^T += dO_b^T P_b, dK^T += Q_b^T dS_b
-  // (one wave per SIMD: nothing else hides the vector work).  Each step is
-  // fenced so the compiler keeps this order.
-  constexpr int kPV = 2 * C::kDBlocks;                 // P.V-like MFMAs per half and product
-  constexpr int kElemPerStep = 16 / C::kSteps;         // vector elements of a half per S step
-  constexpr int kElemPerPV = 16 / kPV;                 // ... per dV/dK MFMA pair
+  constexpr int kPV = 2 * C::kDBlocks;                 // second-product MFMAs per half
+  constexpr int kElemPerStep = 16 / C::kSteps;         // vector elements of a half per first-product step
+  constexpr int kElemPerPV = 16 / kPV;                 // ... per second-product MFMA
+  static_assert(kPV == C::kSteps, "one second-product MFMA per first-product step");
   // registers r of a half hold query rows 8 (r / 4) + 4 half + r % 4
   auto mask_half = [&](f32x16& s, int r0) {
     const int base = r0 + 4 * half - qv_lo;
@@ -421,29 +431,6 @@ attn_bwd_dkdv_kernel(const BwdParams p) {
       if (rel > qv_span) s[r] = -INFINITY;
     }
   };
-  auto row_vals = [&](int slot, int qh, float (&lv)[16], float (&dd)[16]) {
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const float4 l4 = *(const float4*)&lbuf[slot][32 * qh + 8 * jj + 4 * half];
-      const float4 d4 = *(const float4*)&dbuf[slot][32 * qh + 8 * jj + 4 * half];
-      lv[4 * jj] = l4.x; lv[4 * jj + 1] = l4.y; lv[4 * jj + 2] = l4.z; lv[4 * jj + 3] = l4.w;
-      dd[4 * jj] = d4.x; dd[4 * jj + 1] = d4.y; dd[4 * jj + 2] = d4.z; dd[4 * jj + 3] = d4.w;
-    }
-  };
-  // elements [e0, e0 + cnt) of a half: P, dS and their 16-bit pairs
-  auto vec_elems = [&](const f32x16& s, const f32x16& dp, const float (&lv)[16], const float (&dd)[16], int e0,
-                       int cnt, uint32_t (&pp)[8], uint32_t (&dsp)[8]) {
-#pragma unroll
-    for (int e = e0; e < e0 + cnt; e += 2) {
-      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], cexp, -lv[e]));
-      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e + 1], cexp, -lv[e + 1]));
-      pp[e / 2] = pack2<IN>(p0, p1);
-      dsp[e / 2] = pack2<IN>(p0 * (dp[e] - dd[e]), p1 * (dp[e + 1] - dd[e + 1]));
-    }
-  };
-
-  // Operand reads run one phase ahead of the MFMAs that use them (LDS latency
-  // is otherwise paid on every product with one wave per SIMD).
   auto row_frag = [&](const unsigned char* tile, int qh, int st) {
     return *(const uint4*)(tile + 32 * qh * C::kRow + ka[st]);
   };
@@ -454,106 +441,153 @@ attn_bwd_dkdv_kernel(const BwdParams p) {
     const uint2 w1 = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + va[1][c])));
     return make_uint4(w0.x, w0.y, w1.x, w1.y);
   };
-  auto pv_mfma = [&](f32x16 (&acc)[1][C::kDBlocks], uint4 a, const uint32_t (&pk)[8], int m) {
+  auto pv_mfma = [&](uint4 a, const uint32_t (&pk)[8], int m) {
     const int jj = m / C::kDBlocks, c = m % C::kDBlocks;
     acc[0][c] = mfma_16bit<IN>(a, make_uint4(pk[4 * jj], pk[4 * jj + 1], pk[4 * jj + 2], pk[4 * jj + 3]), acc[0][c]);
   };
-  static_assert(kPV == C::kSteps, "one dV/dK MFMA pair per S step");
+  // elements [e0, e0 + cnt) of a half.  Role A: P = exp2(s c - lse), packed.
+  // Role B: dS = P (dP - D), from P's packed pairs.  `vals`: lse (A) or D (B)
+  // of the tile's rows; registers r of a half hold query rows
+  // 8 (r / 4) + 4 half + r % 4 (read four at a time, when needed).
+  // Role B reads P's pairs from `pin` (the half's two 16-byte groups in LDS),
+  // four pairs at a time.
+  auto elems = [&](auto role_tag, const f32x16& x, const float* vals, int qh, const uint4* pin, int e0, int cnt,
+                   uint32_t (&out)[8]) {
+    float4 rv = make_float4(0.f, 0.f, 0.f, 0.f);
+    uint4 pv = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int e = e0; e < e0 + cnt; e += 2) {
+      if (e == e0 || e % 4 == 0) rv = *(const float4*)&vals[32 * qh + 8 * (e / 4) + 4 * half];
+      const float r0 = (e % 4 == 0) ? rv.x : rv.z;
+      const float r1 = (e % 4 == 0) ? rv.y : rv.w;
+      if constexpr (decltype(role_tag)::value) {
+        if (e == e0 || e % 8 == 0) pv = pin[(e / 8) * 64 + lane];
+        const uint32_t w = (e % 8) / 2 == 0 ? pv.x : (e % 8) / 2 == 1 ? pv.y : (e % 8) / 2 == 2 ? pv.z : pv.w;
+        const float p0 = unpack_lo<IN>(w), p1 = unpack_hi<IN>(w);
+        out[e / 2] = pack2<IN>(p0 * (x[e] - r0), p1 * (x[e + 1] - r1));
+      } else {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], cexp, -r0));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e + 1], cexp, -r1));
+        out[e / 2] = pack2<IN>(p0, p1);
+      }
+    }
+  };
 
-  auto step = [&](int it, int slot, const unsigned char* qc, const unsigned char* oc) {
+  // One 64-row tile (halves a, b of 32 query rows) of one role, in four
+  // phases so each half's vector work runs beside matrix work of the other:
+  //   1. X_a = R_a F^T                  (R = Q, F = K for role A; dO, V for B)
+  //   2. X_b, step by step between the vector work of half a
+  //   3. acc += T_a^T Y_a                (T = dO, Y = P for role A; Q, dS for B)
+  //      between the vector work of half b
+  //   4. acc += T_b^T Y_b
+  // Operand reads run one phase ahead of their MFMAs.  Each step is fenced so
+  // the compiler keeps this order.
+  auto tile_step = [&](auto role_tag, int it, const unsigned char* rows, const unsigned char* trs, int lslot) {
+    constexpr bool kB = decltype(role_tag)::value;
     const int gi = it / qtiles;
     const int q0 = (qt_begin + it - gi * qtiles) * 64;
-    const int kw1s = kw1 > kw0 ? kw1 : kw0 + 1;
-    const bool masked_a = !block_all_visible(q0, min(q0 + 32, n), kw0, kw1s, n, p.causal, p.wl, p.wr);
-    const bool masked_b = !block_all_visible(q0 + 32, min(q0 + 64, n), kw0, kw1s, n, p.causal, p.wl, p.wr);
-    f32x16 sa, dpa, sb, dpb;
+    const float* vals = kB ? dbuf[lslot] : lbuf[lslot];
+    const uint4* pb = &pbuf[it & 1][kw][0][0];
+    bool masked_a = false, masked_b = false;
+    if constexpr (!kB) {
+      const int kw1s = kw1 > kw0 ? kw1 : kw0 + 1;
+      masked_a = !block_all_visible(q0, min(q0 + 32, n), kw0, kw1s, n, p.causal, p.wl, p.wr);
+      masked_b = !block_all_visible(q0 + 32, min(q0 + 64, n), kw0, kw1s, n, p.causal, p.wl, p.wr);
+    }
+    f32x16 xa, xb;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      sa[r] = 0.f; dpa[r] = 0.f; sb[r] = 0.f; dpb[r] = 0.f;
+      xa[r] = 0.f; xb[r] = 0.f;
     }
-    // 1: S_a, dP_a; half b's row fragments read meanwhile
-    uint4 qa[C::kSteps], oa[C::kSteps], qb[C::kSteps], ob[C::kSteps];
+    // 1
+    uint4 ra[C::kSteps], rb[C::kSteps];
 #pragma unroll
-    for (int st = 0; st < C::kSteps; ++st) {
-      qa[st] = row_frag(qc, 0, st);
-      oa[st] = row_frag(oc, 0, st);
-    }
-    float lva[16], dda[16];
-    row_vals(slot, 0, lva, dda);
+    for (int st = 0; st < C::kSteps; ++st) ra[st] = row_frag(rows, 0, st);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int st = 0; st < C::kSteps; ++st) {
-      sa = mfma_16bit<IN>(qa[st], kf[st], sa);      // S = Q K^T (lane = key)
-      dpa = mfma_16bit<IN>(oa[st], vf[st], dpa);    // dP = dO V^T
-      qb[st] = row_frag(qc, 1, st);
-      ob[st] = row_frag(oc, 1, st);
+      xa = mfma_16bit<IN>(ra[st], kvf[st], xa);
+      rb[st] = row_frag(rows, 1, st);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (masked_a) mask_half(sa, q0);
+    if (masked_a) mask_half(xa, q0);
     __builtin_amdgcn_sched_barrier(0);
-    // 2: S_b, dP_b beside half a's vector work; half a's transposed operands read meanwhile
-    uint32_t ppa[8], dsa[8];
-    uint4 tva[kPV], tka[kPV];
+    // 2
+    uint32_t ya[8], yb[8];
+    uint4 ta[kPV], tb[kPV];
 #pragma unroll
     for (int st = 0; st < C::kSteps; ++st) {
-      sb = mfma_16bit<IN>(qb[st], kf[st], sb);
-      dpb = mfma_16bit<IN>(ob[st], vf[st], dpb);
-      tva[st] = tr_frag(oc, 0, st);
-      tka[st] = tr_frag(qc, 0, st);
-      vec_elems(sa, dpa, lva, dda, st * kElemPerStep, kElemPerStep, ppa, dsa);
+      xb = mfma_16bit<IN>(rb[st], kvf[st], xb);
+      ta[st] = tr_frag(trs, 0, st);
+      elems(role_tag, xa, vals, 0, pb, st * kElemPerStep, kElemPerStep, ya);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (masked_b) mask_half(sb, q0 + 32);
+    if (masked_b) mask_half(xb, q0 + 32);
+    if constexpr (!kB) {
+      uint4* pw = &pbuf[it & 1][kw][0][0];
+      pw[0 * 64 + lane] = make_uint4(ya[0], ya[1], ya[2], ya[3]);
+      pw[1 * 64 + lane] = make_uint4(ya[4], ya[5], ya[6], ya[7]);
+    }
     __builtin_amdgcn_sched_barrier(0);
-    // 3: dV^T += dO_a^T P_a, dK^T += Q_a^T dS_a beside half b's vector work
-    float lvb[16], ddb[16];
-    row_vals(slot, 1, lvb, ddb);
-    uint32_t ppb[8], dsb[8];
-    uint4 tvb[kPV], tkb[kPV];
+    // 3
 #pragma unroll
     for (int m = 0; m < kPV; ++m) {
-      pv_mfma(dv, tva[m], ppa, m);
-      pv_mfma(dk, tka[m], dsa, m);
-      tvb[m] = tr_frag(oc, 1, m);
-      tkb[m] = tr_frag(qc, 1, m);
-      vec_elems(sb, dpb, lvb, ddb, m * kElemPerPV, kElemPerPV, ppb, dsb);
+      pv_mfma(ta[m], ya, m);
+      tb[m] = tr_frag(trs, 1, m);
+      elems(role_tag, xb, vals, 1, pb + 2 * 64, m * kElemPerPV, kElemPerPV, yb);
       __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (!kB) {
+      uint4* pw = &pbuf[it & 1][kw][0][0];
+      pw[2 * 64 + lane] = make_uint4(yb[0], yb[1], yb[2], yb[3]);
+      pw[3 * 64 + lane] = make_uint4(yb[4], yb[5], yb[6], yb[7]);
     }
     // 4
 #pragma unroll
-    for (int m = 0; m < kPV; ++m) {
-      pv_mfma(dv, tvb[m], ppb, m);
-      pv_mfma(dk, tkb[m], dsb, m);
-    }
+    for (int m = 0; m < kPV; ++m) pv_mfma(tb[m], yb, m);
     __builtin_amdgcn_sched_barrier(0);
   };
 
+  // Iteration i: role A takes tile i (slot i % 3), role B tile i - 1 (slot
+  // (i - 1) % 3, P from iteration i - 1), the DMA fetches tile i + 1 into slot
+  // (i + 1) % 3; the barrier at its end publishes tile i + 1 and P(i), and
+  // frees slot (i - 1) % 3 for the next fetch.  Slots are named statically
+  // (loop unrolled by three).
+  auto iteration = [&](int i, unsigned char* qa, unsigned char* oa, unsigned char* qb, unsigned char* ob,
+                       unsigned char* qn, unsigned char* on, int sa, int sb, int sn) {
+    if (i + 1 < items) issue(i + 1, qn, on);
+    if (!role_b) {
+      if (i < items) tile_step(BoolTag<false>{}, i, qa, oa, sa);
+    } else {
+      if (i >= 1) tile_step(BoolTag<true>{}, i - 1, ob, qb, sb);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    if (i + 1 < items) commit(sn);
+    __syncthreads();
+  };
   if (items > 0) {
     issue(0, qbuf0, obuf0);
     __builtin_amdgcn_s_waitcnt(0);
     commit(0);
     __syncthreads();
-    int it = 0;
-    for (; it + 1 < items; it += 2) {
-      issue(it + 1, qbuf1, obuf1);
-      step(it, 0, qbuf0, obuf0);
-      __builtin_amdgcn_s_waitcnt(0);
-      commit(1);
-      __syncthreads();
-      if (it + 2 < items) issue(it + 2, qbuf0, obuf0);
-      step(it + 1, 1, qbuf1, obuf1);
-      __builtin_amdgcn_s_waitcnt(0);
-      commit(0);
-      __syncthreads();
+    const int total = items + 1;
+    for (int i = 0; i < total; i += 3) {
+      iteration(i, qbuf0, obuf0, qbuf2, obuf2, qbuf1, obuf1, 0, 2, 1);
+      if (i + 1 >= total) break;
+      iteration(i + 1, qbuf1, obuf1, qbuf0, obuf0, qbuf2, obuf2, 1, 0, 2);
+      if (i + 2 >= total) break;
+      iteration(i + 2, qbuf2, obuf2, qbuf1, obuf1, qbuf0, obuf0, 2, 1, 0);
     }
-    if (it < items) step(it, 0, qbuf0, obuf0);
   }
 
   if (kok) {
-    unsigned char* dkg = (unsigned char*)p.dk + ((int64_t)b * p.dk_sb + (int64_t)hkv * p.dk_sh + (int64_t)key * p.dk_ss) * 2;
-    unsigned char* dvg = (unsigned char*)p.dv + ((int64_t)b * p.dv_sb + (int64_t)hkv * p.dv_sh + (int64_t)key * p.dv_ss) * 2;
-    store_rows<IN, D>(dkg, dk[0], p.scale, half);
-    store_rows<IN, D>(dvg, dv[0], 1.f, half);
+    if (role_b) {
+      unsigned char* dkg = (unsigned char*)p.dk + ((int64_t)b * p.dk_sb + (int64_t)hkv * p.dk_sh + (int64_t)key * p.dk_ss) * 2;
+      store_rows<IN, D>(dkg, acc[0], p.scale, half);
+    } else {
+      unsigned char* dvg = (unsigned char*)p.dv + ((int64_t)b * p.dv_sb + (int64_t)hkv * p.dv_sh + (int64_t)key * p.dv_ss) * 2;
+      store_rows<IN, D>(dvg, acc[0], 1.f, half);
+    }
   }
 }
 
@@ -568,7 +602,7 @@ static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((attn_bwd_dkdv_kernel<IN, D>), dim3((unsigned)((int64_t)p.k_blocks * p.batch * p.heads_kv)),
-                     block, 0, stream, p);
+                     dim3(512), 0, stream, p);
   return hipGetLastError();
 }
 
