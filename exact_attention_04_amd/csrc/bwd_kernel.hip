@@ -390,9 +390,18 @@ attn_bwd_dkdv_kernel(const BwdParams p) {
   const int qtiles = qt_end - qt_begin;
   const int items = qtiles * p.group;
   float row_val = 0.f;   // lse or D of one query row, staged through a register
-  auto issue = [&](int it, unsigned char* qdst, unsigned char* odst) {
-    const int gi = it / qtiles;
-    const int qt = qt_begin + it - gi * qtiles;
+  // The items in order: query head hkv * group + gi, query tile qt (fastest).
+  struct Cursor {
+    int gi, qt;
+  };
+  auto advance = [&](Cursor& c) {
+    if (++c.qt == qt_end) {
+      c.qt = qt_begin;
+      ++c.gi;
+    }
+  };
+  auto issue = [&](Cursor c, unsigned char* qdst, unsigned char* odst) {
+    const int gi = c.gi, qt = c.qt;
     const int h = hkv * p.group + gi;
     const unsigned char* qg = (const unsigned char*)p.q + ((int64_t)b * p.q_sb + (int64_t)h * p.q_sh) * 2;
     const unsigned char* og = (const unsigned char*)p.dout + ((int64_t)b * p.do_sb + (int64_t)h * p.do_sh) * 2;
@@ -450,18 +459,17 @@ attn_bwd_dkdv_kernel(const BwdParams p) {
   // of the tile's rows; registers r of a half hold query rows
   // 8 (r / 4) + 4 half + r % 4 (read four at a time, when needed).
   // Role B reads P's pairs from `pin` (the half's two 16-byte groups in LDS),
-  // four pairs at a time.
+  // four pairs at a time.  `rv` and `pv` carry the values read for element e
+  // with e % 4 == 0 (e % 8 == 0) over the following calls.
   auto elems = [&](auto role_tag, const f32x16& x, const float* vals, int qh, const uint4* pin, int e0, int cnt,
-                   uint32_t (&out)[8]) {
-    float4 rv = make_float4(0.f, 0.f, 0.f, 0.f);
-    uint4 pv = make_uint4(0, 0, 0, 0);
+                   uint32_t (&out)[8], float4& rv, uint4& pv) {
 #pragma unroll
     for (int e = e0; e < e0 + cnt; e += 2) {
-      if (e == e0 || e % 4 == 0) rv = *(const float4*)&vals[32 * qh + 8 * (e / 4) + 4 * half];
+      if (e % 4 == 0) rv = *(const float4*)&vals[32 * qh + 8 * (e / 4) + 4 * half];
       const float r0 = (e % 4 == 0) ? rv.x : rv.z;
       const float r1 = (e % 4 == 0) ? rv.y : rv.w;
       if constexpr (decltype(role_tag)::value) {
-        if (e == e0 || e % 8 == 0) pv = pin[(e / 8) * 64 + lane];
+        if (e % 8 == 0) pv = pin[(e / 8) * 64 + lane];
         const uint32_t w = (e % 8) / 2 == 0 ? pv.x : (e % 8) / 2 == 1 ? pv.y : (e % 8) / 2 == 2 ? pv.z : pv.w;
         const float p0 = unpack_lo<IN>(w), p1 = unpack_hi<IN>(w);
         out[e / 2] = pack2<IN>(p0 * (x[e] - r0), p1 * (x[e + 1] - r1));
@@ -480,14 +488,16 @@ attn_bwd_dkdv_kernel(const BwdParams p) {
   //   3. acc += T_a^T Y_a                (T = dO, Y = P for role A; Q, dS for B)
   //      between the vector work of half b
   //   4. acc += T_b^T Y_b
-  // Operand reads run one phase ahead of their MFMAs.  Each step is fenced so
-  // the compiler keeps this order.
-  auto tile_step = [&](auto role_tag, int it, const unsigned char* rows, const unsigned char* trs, int lslot) {
+  // Operand reads run one phase ahead of their MFMAs, and a half's vector
+  // work starts kLag MFMA steps after its accumulator's last MFMA (whose
+  // result it waits for otherwise).  Each step is fenced so the compiler
+  // keeps this order.  `par`: the tile's parity (its P buffer), `q0`: its
+  // first query row.
+  constexpr int kLag = 2;
+  auto tile_step = [&](auto role_tag, int par, int q0, const unsigned char* rows, const unsigned char* trs, int lslot) {
     constexpr bool kB = decltype(role_tag)::value;
-    const int gi = it / qtiles;
-    const int q0 = (qt_begin + it - gi * qtiles) * 64;
     const float* vals = kB ? dbuf[lslot] : lbuf[lslot];
-    const uint4* pb = &pbuf[it & 1][kw][0][0];
+    const uint4* pb = &pbuf[par][kw][0][0];
     bool masked_a = false, masked_b = false;
     if constexpr (!kB) {
       const int kw1s = kw1 > kw0 ? kw1 : kw0 + 1;
@@ -510,42 +520,53 @@ attn_bwd_dkdv_kernel(const BwdParams p) {
       rb[st] = row_frag(rows, 1, st);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (masked_a) mask_half(xa, q0);
-    __builtin_amdgcn_sched_barrier(0);
-    // 2
+    // 2: X_b; half a's vector work from step kLag on
     uint32_t ya[8], yb[8];
     uint4 ta[kPV], tb[kPV];
+    float4 rva = make_float4(0.f, 0.f, 0.f, 0.f), rvb = rva;
+    uint4 pva = make_uint4(0, 0, 0, 0), pvb = pva;
 #pragma unroll
     for (int st = 0; st < C::kSteps; ++st) {
       xb = mfma_16bit<IN>(rb[st], kvf[st], xb);
       ta[st] = tr_frag(trs, 0, st);
-      elems(role_tag, xa, vals, 0, pb, st * kElemPerStep, kElemPerStep, ya);
+      if (st == kLag && masked_a) mask_half(xa, q0);
+      if (st >= kLag) elems(role_tag, xa, vals, 0, pb, (st - kLag) * kElemPerStep, kElemPerStep, ya, rva, pva);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (masked_b) mask_half(xb, q0 + 32);
-    if constexpr (!kB) {
-      uint4* pw = &pbuf[it & 1][kw][0][0];
-      pw[0 * 64 + lane] = make_uint4(ya[0], ya[1], ya[2], ya[3]);
-      pw[1 * 64 + lane] = make_uint4(ya[4], ya[5], ya[6], ya[7]);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // 3
+    // 3: acc += T_a^T Y_a; the rest of half a's vector work, then half b's
+    // from step kLag on (the MFMAs that need Y_a's last elements come after
+    // step kLag)
+    // (the MFMAs of steps < kLag read elements 0-7 only, all done in phase 2)
+    static_assert(kLag <= C::kDBlocks && (C::kSteps - kLag) * kElemPerStep >= 8 && (kPV - kLag) * kElemPerPV >= 8,
+                  "lagged vector work");
 #pragma unroll
     for (int m = 0; m < kPV; ++m) {
+      if (m < kLag)
+        elems(role_tag, xa, vals, 0, pb, (C::kSteps - kLag + m) * kElemPerStep, kElemPerStep, ya, rva, pva);
       pv_mfma(ta[m], ya, m);
       tb[m] = tr_frag(trs, 1, m);
-      elems(role_tag, xb, vals, 1, pb + 2 * 64, m * kElemPerPV, kElemPerPV, yb);
+      if (m == kLag && masked_b) mask_half(xb, q0 + 32);
+      if (m >= kLag) elems(role_tag, xb, vals, 1, pb + 2 * 64, (m - kLag) * kElemPerPV, kElemPerPV, yb, rvb, pvb);
+      if (!kB && m == kLag - 1) {
+        uint4* pw = &pbuf[par][kw][0][0];
+        pw[0 * 64 + lane] = make_uint4(ya[0], ya[1], ya[2], ya[3]);
+        pw[1 * 64 + lane] = make_uint4(ya[4], ya[5], ya[6], ya[7]);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
-    if constexpr (!kB) {
-      uint4* pw = &pbuf[it & 1][kw][0][0];
-      pw[2 * 64 + lane] = make_uint4(yb[0], yb[1], yb[2], yb[3]);
-      pw[3 * 64 + lane] = make_uint4(yb[4], yb[5], yb[6], yb[7]);
-    }
-    // 4
+    // 4: acc += T_b^T Y_b, after the rest of half b's vector work
 #pragma unroll
-    for (int m = 0; m < kPV; ++m) pv_mfma(tb[m], yb, m);
-    __builtin_amdgcn_sched_barrier(0);
+    for (int m = 0; m < kPV; ++m) {
+      if (m < kLag)
+        elems(role_tag, xb, vals, 1, pb + 2 * 64, (kPV - kLag + m) * kElemPerPV, kElemPerPV, yb, rvb, pvb);
+      pv_mfma(tb[m], yb, m);
+      if (!kB && m == kLag - 1) {
+        uint4* pw = &pbuf[par][kw][0][0];
+        pw[2 * 64 + lane] = make_uint4(yb[0], yb[1], yb[2], yb[3]);
+        pw[3 * 64 + lane] = make_uint4(yb[4], yb[5], yb[6], yb[7]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
   // Iteration i: role A takes tile i (slot i % 3), role B tile i - 1 (slot
@@ -553,20 +574,25 @@ attn_bwd_dkdv_kernel(const BwdParams p) {
   // (i + 1) % 3; the barrier at its end publishes tile i + 1 and P(i), and
   // frees slot (i - 1) % 3 for the next fetch.  Slots are named statically
   // (loop unrolled by three).
+  // `nxt`: item i + 1; `cur`: item i.
+  Cursor nxt{0, qt_begin}, cur{0, qt_begin};
   auto iteration = [&](int i, unsigned char* qa, unsigned char* oa, unsigned char* qb, unsigned char* ob,
                        unsigned char* qn, unsigned char* on, int sa, int sb, int sn) {
-    if (i + 1 < items) issue(i + 1, qn, on);
+    if (i + 1 < items) issue(nxt, qn, on);
+    advance(nxt);
     if (!role_b) {
-      if (i < items) tile_step(BoolTag<false>{}, i, qa, oa, sa);
+      if (i < items) tile_step(BoolTag<false>{}, i & 1, cur.qt * 64, qa, oa, sa);
     } else {
-      if (i >= 1) tile_step(BoolTag<true>{}, i - 1, ob, qb, sb);
+      if (i >= 1) tile_step(BoolTag<true>{}, (i - 1) & 1, 0, ob, qb, sb);
     }
+    advance(cur);
     __builtin_amdgcn_s_waitcnt(0);
     if (i + 1 < items) commit(sn);
     __syncthreads();
   };
   if (items > 0) {
-    issue(0, qbuf0, obuf0);
+    issue(nxt, qbuf0, obuf0);
+    advance(nxt);
     __builtin_amdgcn_s_waitcnt(0);
     commit(0);
     __syncthreads();
