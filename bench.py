@@ -121,7 +121,12 @@ def time_gpu(w, steps: int, warmup: int, pv8: bool = False):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     kern_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+
+    def run_once():
+        attention(q, k, v, out=o, lse=lse, **kw)
+
     return {
+        "run": run_once,
         "ms_per_step": (t1 - t0) * 1e3 / steps,
         "kernel_ms_avg": float(np.mean(kern_ms)),
         "kernel_ms_median": float(np.median(kern_ms)),
@@ -205,6 +210,75 @@ def cpu_baseline_bwd(w, target_s: float = 12.0, max_procs: int = 16):
                       f"one process per core; {elapsed:.1f} s wall", "seconds": elapsed}
 
 
+def cold_cache_us(run_once, reps: int = 20, flush_bytes: int = 512 << 20):
+    """Median kernel time with L2 and the MALL flushed before each call (a
+    512 MB device write between calls, outside the timed events)."""
+    import torch
+    buf = torch.empty(flush_bytes // 4, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    times = []
+    for i in range(reps):
+        buf.fill_(float(i))
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        run_once()
+        e.record(stream)
+        torch.cuda.synchronize()
+        times.append(s.elapsed_time(e) * 1e3)
+    del buf
+    return float(np.median(times))
+
+
+def sample_clock(run_once, kernel_ms: float, cap_s: float = 15.0):
+    """GFX clock of each XCD and socket power while the kernel runs back to
+    back: three `amd-smi metric` samples one second apart, after a second of
+    load; medians over the samples (None when the tool is unavailable)."""
+    import shutil
+    import subprocess
+    import threading
+
+    import torch
+    exe = shutil.which("amd-smi") or "/opt/rocm/bin/amd-smi"
+    if not os.path.exists(exe):
+        return None
+    out = {}
+
+    def sampler():
+        try:
+            time.sleep(1.0)   # clocks settle under load first
+            r = subprocess.run([exe, "metric", "-g", "0", "-c", "-p", "-w", "1", "-i", "3", "--json"],
+                               capture_output=True, text=True, timeout=30)
+            out["raw"] = r.stdout
+        except Exception as e:   # the measurement is optional
+            out["err"] = repr(e)
+
+    batch = max(8, int(25.0 / max(kernel_ms, 1e-3)))   # >= 25 ms of work between host syncs
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    t0 = time.time()
+    while th.is_alive() and time.time() - t0 < cap_s:
+        for _ in range(batch):
+            run_once()
+        torch.cuda.synchronize()
+    th.join(timeout=1.0)
+    try:
+        raw, dec, pos, samples = out["raw"], json.JSONDecoder(), 0, []
+        while True:
+            i = raw.find("{", pos)
+            if i < 0:
+                break
+            obj, pos = dec.raw_decode(raw, i)
+            samples.append(obj["gpu_data"][0])
+        mhz = [[float(g["clock"][f"gfx_{x}"]["clk"]["value"]) for x in range(8)] for g in samples]
+        watts = [float(g["power"]["socket_power"]["value"]) for g in samples]
+        per_xcd = [float(v) for v in np.median(np.array(mhz), axis=0)]
+        return {"gfx_mhz": per_xcd, "gfx_mhz_mean": round(float(np.mean(per_xcd)), 1),
+                "socket_power_w": float(np.median(watts)), "samples": len(samples),
+                "tool": "amd-smi metric -g 0 -c -p -w 1 -i 3 while the kernel runs back to back (medians)"}
+    except Exception:
+        return None
+
+
 def copy_calibration(nbytes: int = 1 << 30):
     """A plain device copy of known size, for scaling HBM byte counters."""
     import torch
@@ -273,6 +347,7 @@ def main(argv=None):
                     help="fwd: the forward (the headline metric); bwd: the backward (dQ, dK, dV)")
     ap.add_argument("--pv-dtype", choices=("bf16", "e4m3"), default="bf16",
                     help="fp8 workloads: number format of P and V in the P.V product")
+    ap.add_argument("--no-clock", action="store_true", help="skip the amd-smi clock and power sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (for HBM counter scaling)")
     args = ap.parse_args(argv)
@@ -297,6 +372,18 @@ def main(argv=None):
     g = time_gpu(w, args.steps, args.warmup, pv8)
     if args.copy_calibration:
         copy_calibration()
+    short = flops < 1e11   # the short-sequence workloads: launch- or latency-bound
+    extra = {}
+    if short:
+        bytes_ = workload_bytes(w)
+        extra["short_sequence"] = {
+            "kernel_us_median": round(g["kernel_ms_median"] * 1e3, 2),
+            "kernel_us_min": round(g["kernel_ms_min"] * 1e3, 2),
+            "back_to_back_us": round(g["ms_per_step"] * 1e3, 2),
+            "cold_cache_kernel_us_median": round(cold_cache_us(g["run"]), 2),
+            "algorithmic_GBps_median": round(bytes_ / (g["kernel_ms_median"] * 1e-3) / 1e9, 1),
+        }
+    clock = None if args.no_clock else sample_clock(g["run"], g["kernel_ms_median"])
     value = flops / (g["ms_per_step"] * 1e-3) / 1e12
     achieved = flops / (g["kernel_ms_avg"] * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
@@ -330,12 +417,20 @@ def main(argv=None):
             "kernel": g["plan"].kernel.decode(),
             "kernel_ms_avg": round(g["kernel_ms_avg"], 5),
             "kernel_ms_median": round(g["kernel_ms_median"], 5),
+            "kernel_ms_min": round(g["kernel_ms_min"], 5),
             "flop_per_launch": flops,
             "algorithmic_bytes_per_launch": workload_bytes(w),
             "algorithmic_GBps": round(workload_bytes(w) / (g["kernel_ms_avg"] * 1e-3) / 1e9, 1),
         },
         "cpu_baseline": None,
+        **extra,
+        "clock": clock,
     }
+    if w.dtype == "fp8" and not pv8:
+        # Q.K^T on the fp8 MFMA, P.V on the bf16 MFMA: half the flop at each rate
+        mixed = 1.0 / (0.5 / PEAK_TFLOPS["fp8"] + 0.5 / PEAK_TFLOPS["bf16"])
+        rec["roofline"]["peak_mixed"] = round(mixed, 1)
+        rec["roofline"]["frac_mixed"] = round(achieved / mixed, 4)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, target_s=args.cpu_seconds)
     print(json.dumps(rec), flush=True)
