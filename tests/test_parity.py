@@ -166,3 +166,19 @@ def test_scores_outgrowing_the_first_tile(dtype, causal, scale):
     td = torch_dtype(dtype)
     inp = Inputs(*(_t.from_numpy(x).to(td) for x in (q, k, v)), (1.0, 1.0, 1.0))
     full_check(inp, dtype, causal=causal, scale=scale, what=f"growing scores {dtype} causal={causal} scale={scale}")
+
+
+# ---------------------------------------------------------------------------
+# A long sequence: the last query tiles loop over 4096 key tiles
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("causal,window", [(True, (-1, -1)), (True, (4095, 0))])
+def test_long_sequence_sampled(causal, window):
+    n = 262144
+    inp = small_case(1, 2, n, 128, "bf16", "bshd", 8800 + window[0])
+    o, lse = run_gpu(inp, causal=causal, window=window)
+    assert torch.isfinite(o.float()).all().item()
+    rows = sorted(set(range(0, 40)) | {4095, 4096, 65535, 131072, n // 2 + 7} | set(range(n - 40, n)))
+    r = sampled_check(inp, "bf16", o, lse, [(0, 0), (0, 1)], rows, causal=causal, window=window,
+                      what=f"N={n} window={window}")
+    print(r)
