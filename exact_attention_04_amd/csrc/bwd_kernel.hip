@@ -325,7 +325,7 @@ attn_bwd_dkdv_kernel(const BwdParams p) {
   // P of a tile from role A to role B: [parity][wave pair][16-byte group j][lane]
   __shared__ __attribute__((aligned(1024))) uint4 pbuf[2][4][4][64];
   __shared__ __attribute__((aligned(16))) float lbuf[3][64];   // lse * log2(e) per query row
-  __shared__ __attribute__((aligned(16))) float dbuf[3][64];   // D per query row
+  __shared__ __attribute__((aligned(16))) float dbuf[3][64];   // -D per query row
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -424,7 +424,7 @@ attn_bwd_dkdv_kernel(const BwdParams p) {
   };
   auto commit = [&](int slot) {
     if (tid < 64) lbuf[slot][tid] = __builtin_isfinite(row_val) ? row_val * kLog2e : INFINITY;
-    else if (tid < 128) dbuf[slot][tid - 64] = row_val;
+    else if (tid < 128) dbuf[slot][tid - 64] = -row_val;
   };
 
   constexpr int kPV = 2 * C::kDBlocks;                 // second-product MFMAs per half
@@ -454,10 +454,11 @@ attn_bwd_dkdv_kernel(const BwdParams p) {
     const int jj = m / C::kDBlocks, c = m % C::kDBlocks;
     acc[0][c] = mfma_16bit<IN>(a, make_uint4(pk[4 * jj], pk[4 * jj + 1], pk[4 * jj + 2], pk[4 * jj + 3]), acc[0][c]);
   };
-  // elements [e0, e0 + cnt) of a half.  Role A: P = exp2(s c - lse), packed.
-  // Role B: dS = P (dP - D), from P's packed pairs.  `vals`: lse (A) or D (B)
-  // of the tile's rows; registers r of a half hold query rows
-  // 8 (r / 4) + 4 half + r % 4 (read four at a time, when needed).
+  // elements [e0, e0 + cnt) of a half.  Role A: P = exp2(s c - lse), packed,
+  // with `vals` the lse of the tile's rows (registers r of a half hold query
+  // rows 8 (r / 4) + 4 half + r % 4; read four at a time, when needed).
+  // Role B: dS = P x with x = dP - D (its accumulator started at -D), from
+  // P's packed pairs.
   // Role B reads P's pairs from `pin` (the half's two 16-byte groups in LDS),
   // four pairs at a time.  `rv` and `pv` carry the values read for element e
   // with e % 4 == 0 (e % 8 == 0) over the following calls.
@@ -465,15 +466,15 @@ attn_bwd_dkdv_kernel(const BwdParams p) {
                    uint32_t (&out)[8], float4& rv, uint4& pv) {
 #pragma unroll
     for (int e = e0; e < e0 + cnt; e += 2) {
-      if (e % 4 == 0) rv = *(const float4*)&vals[32 * qh + 8 * (e / 4) + 4 * half];
-      const float r0 = (e % 4 == 0) ? rv.x : rv.z;
-      const float r1 = (e % 4 == 0) ? rv.y : rv.w;
       if constexpr (decltype(role_tag)::value) {
         if (e % 8 == 0) pv = pin[(e / 8) * 64 + lane];
         const uint32_t w = (e % 8) / 2 == 0 ? pv.x : (e % 8) / 2 == 1 ? pv.y : (e % 8) / 2 == 2 ? pv.z : pv.w;
         const float p0 = unpack_lo<IN>(w), p1 = unpack_hi<IN>(w);
-        out[e / 2] = pack2<IN>(p0 * (x[e] - r0), p1 * (x[e + 1] - r1));
+        out[e / 2] = pack2<IN>(p0 * x[e], p1 * x[e + 1]);
       } else {
+        if (e % 4 == 0) rv = *(const float4*)&vals[32 * qh + 8 * (e / 4) + 4 * half];
+        const float r0 = (e % 4 == 0) ? rv.x : rv.z;
+        const float r1 = (e % 4 == 0) ? rv.y : rv.w;
         const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], cexp, -r0));
         const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e + 1], cexp, -r1));
         out[e / 2] = pack2<IN>(p0, p1);
@@ -504,10 +505,15 @@ attn_bwd_dkdv_kernel(const BwdParams p) {
       masked_a = !block_all_visible(q0, min(q0 + 32, n), kw0, kw1s, n, p.causal, p.wl, p.wr);
       masked_b = !block_all_visible(q0 + 32, min(q0 + 64, n), kw0, kw1s, n, p.causal, p.wl, p.wr);
     }
+    // role B's dP accumulators start at -D of their rows (four consecutive
+    // registers hold four consecutive rows), so the MFMAs leave dP - D
     f32x16 xa, xb;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      xa[r] = 0.f; xb[r] = 0.f;
+    for (int jj = 0; jj < 4; ++jj) {
+      const float4 da = kB ? *(const float4*)&vals[8 * jj + 4 * half] : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 db = kB ? *(const float4*)&vals[32 + 8 * jj + 4 * half] : make_float4(0.f, 0.f, 0.f, 0.f);
+      xa[4 * jj] = da.x; xa[4 * jj + 1] = da.y; xa[4 * jj + 2] = da.z; xa[4 * jj + 3] = da.w;
+      xb[4 * jj] = db.x; xb[4 * jj + 1] = db.y; xb[4 * jj + 2] = db.z; xb[4 * jj + 3] = db.w;
     }
     // 1
     uint4 ra[C::kSteps], rb[C::kSteps];
