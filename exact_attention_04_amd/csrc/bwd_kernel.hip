@@ -390,6 +390,12 @@ attn_bwd_dkdv_kernel(const BwdParams p) {
   const int qtiles = qt_end - qt_begin;
   const int items = qtiles * p.group;
   float row_val = 0.f;   // lse or D of one query row, staged through a register
+  // the per-row inputs of this batch, read once: inside the loop the fields
+  // would be fetched by vector loads, and a wait for those would also wait
+  // for the tile DMA issued before them
+  const float* const lse_b = p.lse + (int64_t)b * p.lse_sb;
+  const float* const delta_b = p.delta + (int64_t)b * p.delta_sb;
+  const int64_t lse_sh = p.lse_sh, delta_sh = p.delta_sh;
   // The items in order: query head hkv * group + gi, query tile qt (fastest).
   struct Cursor {
     int gi, qt;
@@ -407,6 +413,13 @@ attn_bwd_dkdv_kernel(const BwdParams p) {
     const unsigned char* og = (const unsigned char*)p.dout + ((int64_t)b * p.do_sb + (int64_t)h * p.do_sh) * 2;
     const Rows64 rq = rows64(qg, q_stride, C::kRow, qt * 64, n);
     const Rows64 ro = rows64(og, o_stride, C::kRow, qt * 64, n);
+    // the row value first: its load is then not queued behind the DMA
+    const int r = qt * 64 + (tid & 63);
+    if (tid < 64) {
+      row_val = r < n ? lse_b[(int64_t)h * lse_sh + r] : INFINITY;
+    } else if (tid < 128) {
+      row_val = r < n ? delta_b[(int64_t)h * delta_sh + r] : 0.f;
+    }
 #pragma unroll
     for (int i = 0; i < kDma; ++i) {
       // (recomputed per tile: a few VALU instead of registers held across the loop)
@@ -414,12 +427,6 @@ attn_bwd_dkdv_kernel(const BwdParams p) {
                       qdst + (wave * kDma + i) * 1024);
       load_16b_to_lds(ro.base, ro.bytes, dma_offset<C::kRow>(wave * kDma + i, lane, o_stride),
                       odst + (wave * kDma + i) * 1024);
-    }
-    const int r = qt * 64 + (tid & 63);
-    if (tid < 64) {
-      row_val = r < n ? p.lse[(int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh + r] : INFINITY;
-    } else if (tid < 128) {
-      row_val = r < n ? p.delta[(int64_t)b * p.delta_sb + (int64_t)h * p.delta_sh + r] : 0.f;
     }
   };
   auto commit = [&](int slot) {
