@@ -30,6 +30,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -71,11 +72,18 @@ def workload_bytes(w) -> float:
     return float((q_elems + 2 * kv_elems) * esz + 2 * q_elems + 4 * w.batch * w.heads * w.seqlen)
 
 
+def kernel_code(text: str) -> str:
+    """Kernel source without `//` comments and blank lines: edits to the
+    comments leave a recorded measurement valid."""
+    lines = (re.sub(r"//.*$", "", line).rstrip() for line in text.splitlines())
+    return "\n".join(line for line in lines if line.strip())
+
+
 def kernel_hash() -> str:
     h = hashlib.sha256()
     for path in KERNEL_SRCS:
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path, encoding="utf-8") as f:
+            h.update(kernel_code(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -20,7 +20,10 @@
 //     the epilogue.
 //   * P^T leaves the accumulator in the B-operand layout of O^T += V^T P^T
 //     (after a 16-bit conversion), so P never touches LDS; V^T fragments come
-//     from LDS with ds_read_b64_tr_b16 and feed every row block.
+//     from LDS with ds_read_b64_tr_b16 and feed every row block.  With fp8
+//     inputs, P is bf16 and V is widened to bf16 on its way into LDS; or
+//     (P8) both stay e4m3 and one v_mfma_scale_f32_32x32x64_f8f6f4 covers a
+//     whole 64-key tile, V^T coming from ds_read_b64_tr_b8.
 //   * Issue is in order per wave, so matrix and vector work overlap only if
 //     they are interleaved in program order: a 64-key tile is processed as
 //     two 32-key halves a, b with
