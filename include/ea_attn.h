@@ -129,7 +129,8 @@ typedef struct ea_attn_plan_info {
   int32_t block_n;           /* keys per K/V tile */
   int32_t waves;             /* wavefronts per workgroup */
   int32_t lds_bytes;         /* LDS per workgroup */
-  int64_t grid;              /* workgroups launched */
+  int64_t grid;              /* workgroups of the unsplit launch (the key split
+                                launches `splits` times as many, then a merge) */
   int64_t kv_tiles;          /* K/V tiles visited over the whole launch */
   int64_t masked_tiles;      /* of which need per-element masking */
   char kernel[64];           /* name of the kernel instantiation */
