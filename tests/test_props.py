@@ -164,3 +164,29 @@ def test_rejects_fp32_inputs():
     q = torch.zeros(1, 8, 1, 64, dtype=torch.float32, device="cuda")
     with pytest.raises(ValueError):
         attention(q, q, q)
+
+
+def test_mixed_layouts_through_the_c_abi_bitwise():
+    # Each tensor has its own strides in ea_attn_args: q and o in BSHD, k and
+    # v in BHSD, v moreover a strided view inside a wider buffer.  The kernel
+    # reads the same values, so the result is bitwise the all-BSHD one.
+    import ctypes
+
+    from exact_attention_04_amd import _lib
+    from exact_attention_04_amd.attention import make_args
+    inp = small_case(2, 4, 300, 128, "bf16", "bshd", 21)
+    q, k, v = _gpu(inp)
+    o_ref, l_ref = attention(q, k, v, causal=True, window_size=(50, 0))
+    k_h = k.permute(0, 2, 1, 3).contiguous()                      # [B, H, N, D]
+    wide = torch.zeros(2, 4, 300, 256, dtype=v.dtype, device="cuda")
+    wide[..., 64:192] = v.permute(0, 2, 1, 3)
+    v_h = wide[..., 64:192]                                       # row stride 256
+    o = torch.empty_like(q)
+    lse = torch.empty_like(l_ref)
+    a = make_args(q, k, v, o, lse, causal=True, window_size=(50, 0))
+    a.k, a.k_stride_b, a.k_stride_s, a.k_stride_h = k_h.data_ptr(), k_h.stride(0), k_h.stride(2), k_h.stride(1)
+    a.v, a.v_stride_b, a.v_stride_s, a.v_stride_h = v_h.data_ptr(), v_h.stride(0), v_h.stride(2), v_h.stride(1)
+    st = _lib.fwd(a, torch.cuda.current_stream().cuda_stream)
+    assert st == 0, _lib.status_string(st)
+    torch.cuda.synchronize()
+    assert _same(o, o_ref) and torch.equal(lse, l_ref)
