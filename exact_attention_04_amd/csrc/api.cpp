@@ -57,6 +57,12 @@ Span span_of(const void* base, int64_t B, int64_t S, int64_t H, int64_t D, int64
 }
 bool overlaps(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
 
+// Span of an fp32 [B, H, N] array with row stride 1.
+Span span_rows_f32(const void* base, int64_t B, int64_t H, int64_t N, int64_t sb, int64_t sh) {
+  const uintptr_t lo = (uintptr_t)base;
+  return Span{lo, lo + (uintptr_t)(((B - 1) * sb + (H - 1) * sh + N) * 4)};
+}
+
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 // Checks shared by ea_attn_fwd and ea_attn_plan.  Returns EA_OK, or the error.
@@ -132,7 +138,8 @@ int validate(const ea_attn_args* a, bool* empty) {
   const int64_t lim = (int64_t)1 << 31;
   if (N >= lim / 2 || B * H >= lim) return EA_EUNSUPPORTED;
   for (int i = 0; i < 4; ++i) {
-    if (strides[3 * i + 1] * N >= lim) return EA_EUNSUPPORTED;
+    // (the first test keeps the products below from overflowing)
+    if (strides[3 * i + 1] >= lim || strides[3 * i + 1] * N >= lim) return EA_EUNSUPPORTED;
     // byte offsets within a 64-row K/V tile are 32-bit
     if (strides[3 * i + 1] * 64 * 2 >= lim) return EA_EUNSUPPORTED;
   }
@@ -142,14 +149,16 @@ int validate(const ea_attn_args* a, bool* empty) {
   const Span sk = span_of(a->k, B, N, Hk, D, a->k_stride_b, a->k_stride_s, a->k_stride_h, ein);
   const Span sv = span_of(a->v, B, N, Hk, D, a->v_stride_b, a->v_stride_s, a->v_stride_h, ein);
   if (overlaps(so, sq) || overlaps(so, sk) || overlaps(so, sv)) return EA_EINVAL;
+  if (a->lse != nullptr) {
+    const Span sl = span_rows_f32(a->lse, B, H, N, a->lse_stride_b, a->lse_stride_h);
+    if (overlaps(sl, so) || overlaps(sl, sq) || overlaps(sl, sk) || overlaps(sl, sv)) return EA_EINVAL;
+  }
   int64_t ws_bytes = 0;
   if (void* ws = workspace_of(a, &ws_bytes)) {
     if (!aligned16(ws)) return EA_EUNSUPPORTED;
     const Span sw{(uintptr_t)ws, (uintptr_t)ws + (uintptr_t)ws_bytes};
     if (overlaps(sw, so) || overlaps(sw, sq) || overlaps(sw, sk) || overlaps(sw, sv)) return EA_EINVAL;
-    if (a->lse != nullptr &&
-        overlaps(sw, Span{(uintptr_t)a->lse, (uintptr_t)a->lse + (uintptr_t)(((B - 1) * a->lse_stride_b +
-                                                                               (H - 1) * a->lse_stride_h + N) * 4)}))
+    if (a->lse != nullptr && overlaps(sw, span_rows_f32(a->lse, B, H, N, a->lse_stride_b, a->lse_stride_h)))
       return EA_EINVAL;
   }
   return EA_OK;
@@ -189,12 +198,6 @@ ea::FwdParams make_params(const ea_attn_args* a, int cfg) {
   p.part_o = nullptr;
   p.part_lse = nullptr;
   return p;
-}
-
-// Span of an fp32 [B, H, N] array with row stride 1.
-Span span_rows_f32(const void* base, int64_t B, int64_t H, int64_t N, int64_t sb, int64_t sh) {
-  const uintptr_t lo = (uintptr_t)base;
-  return Span{lo, lo + (uintptr_t)(((B - 1) * sb + (H - 1) * sh + N) * 4)};
 }
 
 // Checks of ea_attn_bwd.  Returns EA_OK, or the error; sets *empty when there
@@ -238,7 +241,7 @@ int validate_bwd(const ea_attn_bwd_args* a, bool* empty) {
   if (N >= lim / 2 || B * H >= lim) return EA_EUNSUPPORTED;
   if ((N + 127) / 128 * B * H >= lim / 2) return EA_EUNSUPPORTED;
   for (int i = 0; i < 8; ++i) {
-    if (strides[3 * i + 1] * N >= lim) return EA_EUNSUPPORTED;
+    if (strides[3 * i + 1] >= lim || strides[3 * i + 1] * N >= lim) return EA_EUNSUPPORTED;
     if (strides[3 * i + 1] * 64 * 2 >= lim) return EA_EUNSUPPORTED;
   }
   // outputs (dq, dk, dv, delta) overlap neither each other nor any input

@@ -151,7 +151,8 @@ typedef struct ea_attn_plan_info {
  *                    non-finite softmax_scale; a descale that is not finite
  *                    and > 0, or != 1 for 16-bit inputs; window bounds < -1;
  *                    pv_dtype not 0, EA_BF16 or EA_FP8_E4M3, or reserved != 0;
- *                    o overlapping q, k or v.
+ *                    o overlapping q, k or v; lse overlapping o, q, k or v;
+ *                    a workspace overlapping any tensor.
  *   EA_EUNSUPPORTED  float32 inputs; headdim not 64 or 128 (fp8: not 128);
  *                    a nonzero pv_dtype with 16-bit inputs;
  *                    Nq != Nk; Hq not a multiple of Hk; softmax_scale <= 0; an output

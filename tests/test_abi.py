@@ -150,6 +150,10 @@ def test_plan_tile_counts_causal_and_window():
     ("k_stride_s", 128 * 3 + 4, _lib.EA_EUNSUPPORTED),  # row stride not a 16-byte multiple
     ("v_stride_h", -128, _lib.EA_EUNSUPPORTED),
     ("lse", FAKE + 2, _lib.EA_EUNSUPPORTED),
+    ("lse", FAKE + 16, _lib.EA_EINVAL),             # lse inside q
+    ("lse", FAKE + 3 * SIZE + 64, _lib.EA_EINVAL),  # lse inside o
+    # an absurd row stride is refused before any product with it can wrap
+    ("k_stride_s", 1 << 62, _lib.EA_EUNSUPPORTED),
 ])
 def test_validation_errors(field, value, code):
     a = make()
@@ -269,3 +273,64 @@ def test_python_wrapper_rejects_cpu_tensors():
     x = torch.zeros(1, 8, 1, 64, dtype=torch.float16)
     with pytest.raises(ValueError):
         attention(x, x, x)
+
+
+def make_bwd(B=2, N=300, H=3, D=128, **kw):
+    """Backward arguments over fake, disjoint BSHD tensors."""
+    a = _lib.BwdArgs()
+    a.struct_size = ctypes.sizeof(_lib.BwdArgs)
+    a.dtype = _lib.EA_BF16
+    a.window_left = a.window_right = -1
+    a.softmax_scale = 1.0 / math.sqrt(D)
+    a.batch, a.seqlen, a.nheads_q, a.nheads_k, a.headdim = B, N, H, H, D
+    size = B * N * H * D * 4 + 4096
+    for i, t in enumerate(("q", "k", "v", "o", "dout", "lse", "delta", "dq", "dk", "dv")):
+        setattr(a, t, FAKE + i * size)
+    for t in ("q", "k", "v", "o", "do", "dq", "dk", "dv"):
+        setattr(a, f"{t}_stride_b", N * H * D)
+        setattr(a, f"{t}_stride_s", H * D)
+        setattr(a, f"{t}_stride_h", D)
+    a.lse_stride_b = a.delta_stride_b = H * N
+    a.lse_stride_h = a.delta_stride_h = N
+    for k_, v_ in kw.items():
+        setattr(a, k_, v_)
+    return a
+
+
+BWD_SIZE = 2 * 300 * 3 * 128 * 4 + 4096   # make_bwd()'s spacing of the fake tensors
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("struct_size", 8, _lib.EA_EINVAL),
+    ("seqlen", -1, _lib.EA_EINVAL),
+    ("nheads_k", 0, _lib.EA_EINVAL),
+    ("softmax_scale", float("nan"), _lib.EA_EINVAL),
+    ("window_right", -2, _lib.EA_EINVAL),
+    ("dv", 0, _lib.EA_EINVAL),
+    ("dq", FAKE + 64, _lib.EA_EINVAL),                  # dq inside q
+    ("dk", FAKE + 7 * BWD_SIZE, _lib.EA_EINVAL),        # dk on top of dq
+    ("delta", FAKE + 5 * BWD_SIZE, _lib.EA_EINVAL),     # delta on top of lse
+    ("dtype", _lib.EA_FP8_E4M3, _lib.EA_EUNSUPPORTED),  # forward only in fp8
+    ("dtype", _lib.EA_F32, _lib.EA_EUNSUPPORTED),
+    ("headdim", 80, _lib.EA_EUNSUPPORTED),
+    ("nheads_k", 2, _lib.EA_EUNSUPPORTED),
+    ("softmax_scale", 0.0, _lib.EA_EUNSUPPORTED),
+    ("dout", FAKE + 4 * BWD_SIZE + 8, _lib.EA_EUNSUPPORTED),   # not 16-byte aligned
+    ("lse", FAKE + 5 * BWD_SIZE + 2, _lib.EA_EUNSUPPORTED),    # not 4-byte aligned
+    ("q_stride_s", 3 * 128 + 4, _lib.EA_EUNSUPPORTED),
+    ("dk_stride_h", -128, _lib.EA_EUNSUPPORTED),
+    ("v_stride_s", 1 << 62, _lib.EA_EUNSUPPORTED),
+])
+def test_bwd_validation_errors(field, value, code):
+    # every failing check returns before a device is queried
+    a = make_bwd()
+    setattr(a, field, value)
+    assert _lib.lib().ea_attn_bwd(ctypes.byref(a), None) == code, (field, value)
+
+
+def test_bwd_empty_problem_is_ok_without_pointers():
+    for fields in ({"batch": 0}, {"seqlen": 0}):
+        a = make_bwd(**fields)
+        for t in ("q", "k", "v", "o", "dout", "lse", "delta", "dq", "dk", "dv"):
+            setattr(a, t, 0)
+        assert _lib.lib().ea_attn_bwd(ctypes.byref(a), None) == _lib.EA_OK
