@@ -41,6 +41,21 @@ def _dims(x: torch.Tensor, layout: str):
     raise ValueError(f"layout must be 'bshd' or 'bhsd', got {layout!r}")
 
 
+def _check_buffer(name: str, t: torch.Tensor, shape, dtype: torch.dtype, device: torch.device) -> None:
+    """A caller-supplied output: the kernels write it in full, so its shape,
+    dtype and device must be the ones the call produces."""
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != device:
+        raise ValueError(f"{name} must be a {dtype} tensor of shape {tuple(shape)} on {device}, "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+
+
+def _check_rows(name: str, t: torch.Tensor, B: int, H: int, N: int, device: torch.device) -> None:
+    """A float32 [B, H, N] per-row array (LSE, delta) with contiguous rows."""
+    _check_buffer(name, t, (B, H, N), torch.float32, device)
+    if N > 1 and t.stride(2) != 1:
+        raise ValueError(f"{name} rows must be contiguous (stride 1 along the sequence)")
+
+
 def make_args(q, k, v, o, lse, *, causal=False, window_size=(-1, -1), softmax_scale=None,
               layout="bshd", descale=None, pv_dtype=None) -> _lib.AttnArgs:
     """Fill an ``ea_attn_args`` for the given tensors (no checks beyond shapes)."""
@@ -116,13 +131,19 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not t.is_cuda:
             raise ValueError(f"{name} must be a GPU tensor (this library has no CPU path)")
+        if t.device != q.device:
+            raise ValueError(f"{name} is on {t.device}, q on {q.device}")
     (B, N, H, _), _ = _dims(q, layout)
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype_for(q.dtype), device=q.device)
-    if return_lse and lse is None:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    else:
+        _check_buffer("out", out, q.shape, out_dtype_for(q.dtype), q.device)
     if not return_lse:
         lse = None
+    elif lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    else:
+        _check_rows("lse", lse, B, H, N, q.device)
     a = make_args(q, k, v, out, lse, causal=causal, window_size=window_size, softmax_scale=softmax_scale,
                   layout=layout, descale=descale, pv_dtype=pv_dtype)
     stream = torch.cuda.current_stream(q.device).cuda_stream
@@ -156,17 +177,26 @@ def attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: tor
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("lse", lse)):
         if not t.is_cuda:
             raise ValueError(f"{name} must be a GPU tensor (this library has no CPU path)")
+        if t.device != q.device:
+            raise ValueError(f"{name} is on {t.device}, q on {q.device}")
     if q.dtype not in (torch.float16, torch.bfloat16) or any(t.dtype != q.dtype for t in (k, v, o, dout)):
         raise ValueError("the backward takes float16 or bfloat16 q, k, v, o, dout of one dtype")
     (B, N, H, D), (qb, qs, qh) = _dims(q, layout)
     (Bk, Nk, Hk, Dk), (kb, ks, kh) = _dims(k, layout)
     if Bk != B or Nk != N or Dk != D or tuple(v.shape) != tuple(k.shape) or tuple(o.shape) != tuple(q.shape) \
-            or tuple(dout.shape) != tuple(q.shape) or tuple(lse.shape) != (B, H, N):
-        raise ValueError("shape mismatch between q, k, v, o, dout, lse")
+            or tuple(dout.shape) != tuple(q.shape):
+        raise ValueError("shape mismatch between q, k, v, o, dout")
+    _check_rows("lse", lse, B, H, N, q.device)
+    for name, t, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if t is not None:
+            _check_buffer(name, t, like.shape, like.dtype, q.device)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if delta is None else delta
+    if delta is None:
+        delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    else:
+        _check_rows("delta", delta, B, H, N, q.device)
     a = _lib.BwdArgs()
     a.struct_size = _lib.ctypes.sizeof(_lib.BwdArgs)
     a.dtype = _DTYPES[q.dtype]
@@ -182,8 +212,6 @@ def attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: tor
     a.q, a.k, a.v, a.o, a.dout = q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr()
     a.dq, a.dk, a.dv = dq.data_ptr(), dk.data_ptr(), dv.data_ptr()
     a.lse, a.delta = lse.data_ptr(), delta.data_ptr()
-    if lse.stride(2) != 1 or delta.stride(2) != 1:
-        raise ValueError("lse and delta rows must be contiguous")
     a.lse_stride_b, a.lse_stride_h = lse.stride(0), lse.stride(1)
     a.delta_stride_b, a.delta_stride_h = delta.stride(0), delta.stride(1)
     stream = torch.cuda.current_stream(q.device).cuda_stream

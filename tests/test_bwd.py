@@ -196,3 +196,16 @@ def test_bwd_empty_and_errors():
         attention_backward(q.float(), q.float(), q.float(), q.float(), q.float(), lse)
     with pytest.raises(ValueError):   # k and v with different head counts
         attention_backward(q, q[:, :, :1].expand(1, 8, 3, 64), q, q, q, lse)
+    # caller buffers must match what the kernels write (and lse must be fp32)
+    f32 = dict(dtype=torch.float32, device="cuda")
+    bad = [
+        dict(dq=torch.empty(1, 8, 2, 32, dtype=torch.float16, device="cuda")),
+        dict(dk=torch.empty(1, 8, 2, 64, dtype=torch.bfloat16, device="cuda")),
+        dict(delta=torch.empty(1, 2, 8, dtype=torch.float16, device="cuda")),
+        dict(delta=torch.empty(1, 8, 2, **f32).transpose(1, 2)),
+    ]
+    for kw in bad:
+        with pytest.raises(ValueError):
+            attention_backward(q, q, q, q, q, lse, **kw)
+    with pytest.raises(ValueError):
+        attention_backward(q, q, q, q, q, lse.to(torch.bfloat16))

@@ -190,3 +190,24 @@ def test_mixed_layouts_through_the_c_abi_bitwise():
     assert st == 0, _lib.status_string(st)
     torch.cuda.synchronize()
     assert _same(o, o_ref) and torch.equal(lse, l_ref)
+
+
+def test_wrapper_refuses_mismatched_output_buffers():
+    # the kernels write out and lse in full: a caller's buffers must match
+    q = torch.zeros(1, 64, 2, 64, dtype=torch.float16, device="cuda")
+    f32 = dict(dtype=torch.float32, device="cuda")
+    bad = [
+        dict(out=torch.empty(1, 64, 2, 32, dtype=torch.float16, device="cuda")),
+        dict(out=torch.empty(1, 64, 2, 64, dtype=torch.bfloat16, device="cuda")),
+        dict(lse=torch.empty(1, 2, 63, **f32)),
+        dict(lse=torch.empty(1, 2, 64, dtype=torch.float16, device="cuda")),
+        dict(lse=torch.empty(1, 64, 2, **f32).transpose(1, 2)),   # rows not contiguous
+    ]
+    for kw in bad:
+        with pytest.raises(ValueError):
+            attention(q, q, q, **kw)
+    o, lse = attention(q, q, q, out=torch.empty_like(q), lse=torch.empty(1, 2, 64, **f32))
+    torch.cuda.synchronize()
+    # q = k = 0: every weight is equal, so O is the mean of V (all zero) and LSE = ln 64
+    assert torch.equal(o, torch.zeros_like(o))
+    assert torch.allclose(lse, torch.full_like(lse, float(np.log(64.0))), atol=1e-5)
