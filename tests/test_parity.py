@@ -146,6 +146,26 @@ def test_key_split_masks(n, d, dtype, mask):
     full_check(inp, dtype, causal=causal, window=window, what=f"split {dtype} n{n} {mask}", split_kv=True)
 
 
+@pytest.mark.parametrize("window", [(-1, -1), (1000, -1)])
+@pytest.mark.parametrize("layout", ["bshd", "bhsd"])
+@pytest.mark.parametrize("dtype,d,heads,heads_kv", [("bf16", 128, 8, 2), ("f16", 64, 4, 1)])
+def test_key_split_with_shared_kv_heads(dtype, d, heads, heads_kv, layout, window):
+    # causal launches the planner does split (plain, and with a window of
+    # 1000 keys that still leaves the tiles unbalanced), with query heads
+    # sharing K/V heads
+    from exact_attention_04_amd import plan
+    from parity_helpers import upload
+    causal = True
+    inp = small_case(1, heads, 1100, d, dtype, layout, 8100 + heads + d, heads_kv=heads_kv)
+    q, k, v = upload(inp)
+    o = torch.empty_like(q)
+    (B, N, H) = (1, 1100, heads)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    assert plan(q, k, v, o, lse, causal=causal, window_size=window, layout=layout).splits > 1
+    full_check(inp, dtype, causal=causal, window=window, layout=layout, split_kv=True,
+               what=f"split {dtype} H{heads}/Hk{heads_kv} {layout} window {window}")
+
+
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("scale", [1.0, 2.0])
