@@ -69,3 +69,24 @@ def test_more_than_one_gpu_is_refused(capsys):
 def test_e4m3_pv_needs_an_fp8_workload(capsys):
     assert bench.main(["--pv-dtype", "e4m3"]) == 2
     assert "fp8" in capsys.readouterr().err
+
+
+def test_kernel_hash_ignores_comments_only():
+    code = "int f(int x) {\n  return x + 1;  // add one\n}\n"
+    recommented = "// a header comment\nint f(int x) {\n\n  return x + 1;  // a different note\n}\n"
+    changed = "int f(int x) {\n  return x + 2;  // add one\n}\n"
+    assert bench.kernel_code(code) == bench.kernel_code(recommented)
+    assert bench.kernel_code(code) != bench.kernel_code(changed)
+
+
+@pytest.mark.parametrize("name", ["sdpa_b4h32n4096d128_bf16_causal", "fp8_b1h16n65536d128_causal_pv8"])
+def test_traffic_records_are_well_formed(name):
+    # a committed HBM-traffic record: keyed by a 16-hex source hash, and at
+    # least the one-pass algorithmic bytes (a kernel cannot read less)
+    import json
+    import os
+    with open(os.path.join(bench.ROOT, "profiles", f"traffic_{name}.json")) as f:
+        rec = json.load(f)
+    assert len(rec["kernel_sha256_16"]) == 16 and int(rec["kernel_sha256_16"], 16) >= 0
+    w = WORKLOADS[name.replace("_pv8", "")]
+    assert rec["hbm_bytes_per_launch"] >= bench.workload_bytes(w)
