@@ -370,3 +370,51 @@ def test_planted_mistakes_are_caught(monkeypatch, mutation):
         o, lse = sdpa_fp64.attention_head(q, k, v, scale, True)
     caught = not (np.allclose(o, ob, rtol=0, atol=1e-13, equal_nan=True) and np.allclose(lse, lb, rtol=0, atol=1e-13, equal_nan=True))
     assert caught, f"planted mistake {mutation} slipped past the brute-force pin"
+
+
+# ---------------------------------------------------------------------------
+# The probability matrix (the backward tests' error bounds are built from it)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("causal,wl,wr", MASKS)
+@pytest.mark.parametrize("n,nk,d", [(1, 1, 1), (5, 5, 3), (9, 9, 8), (16, 16, 4), (6, 11, 5)])
+def test_probabilities_against_brute_force(n, nk, d, causal, wl, wr):
+    # With V the identity, the definition's output row i is P's row i
+    # (O_ic = sum_j P_ij [j == c]), so the brute force over pure-Python loops
+    # gives P element by element.
+    rng = np.random.default_rng(100 + 7 * n + nk + d)
+    q, k, _ = rand_head(rng, n, d, nk)
+    scale = 0.7
+    pb, _ = brute_force(q.tolist(), k.tolist(), np.eye(nk).tolist(), scale, causal, wl, wr)
+    p = oracle.attention_probs_head(q, k, scale, causal, wl, wr)
+    assert p.shape == (n, nk)
+    np.testing.assert_allclose(p, pb, rtol=0, atol=1e-14)
+
+
+def test_probabilities_reproduce_the_output():
+    # P V is the oracle's O for an arbitrary V, and P's row i is LSE's softmax
+    rng = np.random.default_rng(23)
+    q, k, v = rand_head(rng, 37, 6)
+    for causal, wl, wr in MASKS:
+        p = oracle.attention_probs_head(q, k, 0.45, causal, wl, wr)
+        o, lse = oracle.attention_head(q, k, v, 0.45, causal, wl, wr)
+        np.testing.assert_allclose(p @ v, o, rtol=0, atol=1e-13)
+        s = 0.45 * (q @ k.T)
+        vis = p > 0
+        np.testing.assert_allclose(p[vis], np.exp(s - lse[:, None])[vis], rtol=1e-13, atol=0)
+
+
+@pytest.mark.parametrize("mutation", ["scale_dropped", "transposed", "unnormalised"])
+def test_planted_probability_mistakes_are_caught(monkeypatch, mutation):
+    rng = np.random.default_rng(15)
+    q, k, _ = rand_head(rng, 9, 4)
+    scale = 0.8
+    pb, _ = brute_force(q.tolist(), k.tolist(), np.eye(9).tolist(), scale, True, -1, -1)
+    if mutation == "scale_dropped":
+        p = sdpa_fp64.attention_probs_head(q, k, 1.0, True)
+    elif mutation == "transposed":
+        p = sdpa_fp64.attention_probs_head(k, q, scale, True)
+    else:
+        monkeypatch.setattr(sdpa_fp64, "_softmax_block", _buggy_softmax_no_norm)
+        p = sdpa_fp64.attention_probs_head(q, k, scale, True)
+    assert not np.allclose(p, pb, rtol=0, atol=1e-14), f"planted mistake {mutation} slipped past the pin"
