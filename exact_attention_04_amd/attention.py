@@ -56,6 +56,22 @@ def _check_rows(name: str, t: torch.Tensor, B: int, H: int, N: int, device: torc
         raise ValueError(f"{name} rows must be contiguous (stride 1 along the sequence)")
 
 
+_INT32_MAX = 2 ** 31 - 1
+
+
+def _window(window_size) -> Tuple[int, int]:
+    """The window bounds as C int32 values.  -1 means unbounded; a bound past
+    int32 reaches beyond any sequence the library accepts, so it is passed as
+    the largest int32 (the library treats a bound >= N as unbounded too)."""
+    out = []
+    for w in window_size:
+        w = int(w)
+        if w < -1:
+            raise ValueError(f"window bounds must be >= -1, got {tuple(window_size)}")
+        out.append(min(w, _INT32_MAX))
+    return out[0], out[1]
+
+
 def make_args(q, k, v, o, lse, *, causal=False, window_size=(-1, -1), softmax_scale=None,
               layout="bshd", descale=None, pv_dtype=None) -> _lib.AttnArgs:
     """Fill an ``ea_attn_args`` for the given tensors (no checks beyond shapes)."""
@@ -72,7 +88,7 @@ def make_args(q, k, v, o, lse, *, causal=False, window_size=(-1, -1), softmax_sc
     a.in_dtype = _DTYPES[q.dtype]
     a.out_dtype = _DTYPES.get(o.dtype, 0)
     a.causal = 1 if causal else 0
-    a.window_left, a.window_right = int(window_size[0]), int(window_size[1])
+    a.window_left, a.window_right = _window(window_size)
     a.softmax_scale = float(1.0 / math.sqrt(D) if softmax_scale is None else softmax_scale)
     dq, dk, dv = (1.0, 1.0, 1.0) if descale is None else descale
     a.q_descale, a.k_descale, a.v_descale = float(dq), float(dk), float(dv)
@@ -201,7 +217,7 @@ def attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: tor
     a.struct_size = _lib.ctypes.sizeof(_lib.BwdArgs)
     a.dtype = _DTYPES[q.dtype]
     a.causal = 1 if causal else 0
-    a.window_left, a.window_right = int(window_size[0]), int(window_size[1])
+    a.window_left, a.window_right = _window(window_size)
     a.softmax_scale = float(1.0 / math.sqrt(D) if softmax_scale is None else softmax_scale)
     a.batch, a.seqlen, a.nheads_q, a.nheads_k, a.headdim = B, N, H, Hk, D
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", dout), ("dq", dq), ("dk", dk), ("dv", dv)):

@@ -45,23 +45,54 @@ int elem_bytes(int dtype) {
   }
 }
 
-// Byte range [lo, hi) spanned by a [B, S, H, D] strided tensor (strides >= 0).
+// Largest byte extent accepted for one tensor (128 TiB, beyond any device
+// allocation): with it, every offset the kernels form fits in int64 and a
+// base pointer plus its extent cannot wrap.
+constexpr int64_t kMaxExtentBytes = (int64_t)1 << 47;
+
+// Byte extent of a [B, S, H, D] strided tensor (strides >= 0, sizes >= 1):
+// (B-1) sb + (S-1) ss + (H-1) sh + D elements of `esz` bytes.  False when it
+// overflows or exceeds kMaxExtentBytes.
+bool extent_of(int64_t B, int64_t S, int64_t H, int64_t D, int64_t sb, int64_t ss, int64_t sh, int esz,
+               int64_t* bytes) {
+  int64_t t0 = 0, t1 = 0, t2 = 0, sum = 0, out = 0;
+  if (__builtin_mul_overflow(B - 1, sb, &t0) || __builtin_mul_overflow(S - 1, ss, &t1) ||
+      __builtin_mul_overflow(H - 1, sh, &t2) || __builtin_add_overflow(t0, t1, &sum) ||
+      __builtin_add_overflow(sum, t2, &sum) || __builtin_add_overflow(sum, D, &sum) ||
+      __builtin_mul_overflow(sum, (int64_t)esz, &out) || out > kMaxExtentBytes)
+    return false;
+  *bytes = out;
+  return true;
+}
+
+// Byte range [lo, hi) spanned by a tensor whose extent passed extent_of.
 struct Span {
   uintptr_t lo, hi;
 };
+Span span_at(const void* base, int64_t bytes) {
+  const uintptr_t lo = (uintptr_t)base;
+  return {lo, lo + (uintptr_t)bytes};
+}
 Span span_of(const void* base, int64_t B, int64_t S, int64_t H, int64_t D, int64_t sb, int64_t ss, int64_t sh,
              int esz) {
-  const int64_t last = (B - 1) * sb + (S - 1) * ss + (H - 1) * sh + D;
-  const uintptr_t lo = (uintptr_t)base;
-  return {lo, lo + (uintptr_t)(last * esz)};
+  int64_t bytes = 0;
+  extent_of(B, S, H, D, sb, ss, sh, esz, &bytes);
+  return span_at(base, bytes);
 }
 bool overlaps(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
 
 // Span of an fp32 [B, H, N] array with row stride 1.
 Span span_rows_f32(const void* base, int64_t B, int64_t H, int64_t N, int64_t sb, int64_t sh) {
-  const uintptr_t lo = (uintptr_t)base;
-  return Span{lo, lo + (uintptr_t)(((B - 1) * sb + (H - 1) * sh + N) * 4)};
+  return span_of(base, B, 1, H, N, sb, 0, sh, 4);
 }
+bool rows_f32_fit(int64_t B, int64_t H, int64_t N, int64_t sb, int64_t sh) {
+  int64_t bytes = 0;
+  return extent_of(B, 1, H, N, sb, 0, sh, 4, &bytes);
+}
+
+// A window bound at or past the sequence length bounds nothing: it is
+// treated as -1, which keeps the kernels' row + bound sums within int32.
+int32_t effective_window(int32_t w, int64_t n) { return (int64_t)w >= n ? -1 : w; }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -126,7 +157,7 @@ int validate(const ea_attn_args* a, bool* empty) {
   const int64_t strides[12] = {a->q_stride_b, a->q_stride_s, a->q_stride_h, a->k_stride_b, a->k_stride_s, a->k_stride_h,
                                a->v_stride_b, a->v_stride_s, a->v_stride_h, a->o_stride_b, a->o_stride_s, a->o_stride_h};
   for (int i = 0; i < 12; ++i) {
-    if (strides[i] < 0) return EA_EUNSUPPORTED;
+    if (strides[i] < 0 || strides[i] > kMaxExtentBytes) return EA_EUNSUPPORTED;
     const int esz = i < 9 ? ein : eout;
     if ((strides[i] * esz) % 16 != 0) return EA_EUNSUPPORTED;
   }
@@ -136,7 +167,8 @@ int validate(const ea_attn_args* a, bool* empty) {
   }
   // the kernels keep per-head row offsets and tile indices in 32 bits
   const int64_t lim = (int64_t)1 << 31;
-  if (N >= lim / 2 || B * H >= lim) return EA_EUNSUPPORTED;
+  int64_t bh = 0;
+  if (N >= lim / 2 || __builtin_mul_overflow(B, H, &bh) || bh >= lim) return EA_EUNSUPPORTED;
   for (int i = 0; i < 4; ++i) {
     // (the first test keeps the products below from overflowing)
     if (strides[3 * i + 1] >= lim || strides[3 * i + 1] * N >= lim) return EA_EUNSUPPORTED;
@@ -144,6 +176,18 @@ int validate(const ea_attn_args* a, bool* empty) {
     if (strides[3 * i + 1] * 64 * 2 >= lim) return EA_EUNSUPPORTED;
   }
 
+  // every tensor's extent is bounded before any span is formed
+  {
+    int64_t bytes = 0;
+    const int64_t heads[4] = {H, Hk, Hk, H};
+    for (int i = 0; i < 4; ++i)
+      if (!extent_of(B, N, heads[i], D, strides[3 * i], strides[3 * i + 1], strides[3 * i + 2], i < 3 ? ein : eout,
+                     &bytes))
+        return EA_EUNSUPPORTED;
+    if (a->lse != nullptr && !rows_f32_fit(B, H, N, a->lse_stride_b, a->lse_stride_h)) return EA_EUNSUPPORTED;
+    if (a->struct_size >= kArgsV2Size && a->workspace != nullptr && a->workspace_bytes > kMaxExtentBytes)
+      return EA_EUNSUPPORTED;
+  }
   const Span so = span_of(a->o, B, N, H, D, a->o_stride_b, a->o_stride_s, a->o_stride_h, eout);
   const Span sq = span_of(a->q, B, N, H, D, a->q_stride_b, a->q_stride_s, a->q_stride_h, ein);
   const Span sk = span_of(a->k, B, N, Hk, D, a->k_stride_b, a->k_stride_s, a->k_stride_h, ein);
@@ -187,8 +231,8 @@ ea::FwdParams make_params(const ea_attn_args* a, int cfg) {
   p.o_sb = a->o_stride_b; p.o_ss = a->o_stride_s; p.o_sh = a->o_stride_h;
   p.lse_sb = a->lse_stride_b; p.lse_sh = a->lse_stride_h;
   p.causal = a->causal ? 1 : 0;
-  p.wl = a->window_left;
-  p.wr = a->window_right;
+  p.wl = effective_window(a->window_left, a->seqlen_q);
+  p.wr = effective_window(a->window_right, a->seqlen_q);
   const bool fp8 = a->in_dtype == EA_FP8_E4M3;
   const double c = (double)a->softmax_scale * (fp8 ? (double)a->q_descale * (double)a->k_descale : 1.0) *
                    1.4426950408889634;
@@ -227,7 +271,7 @@ int validate_bwd(const ea_attn_bwd_args* a, bool* empty) {
                                a->do_stride_b, a->do_stride_s, a->do_stride_h, a->dq_stride_b, a->dq_stride_s, a->dq_stride_h,
                                a->dk_stride_b, a->dk_stride_s, a->dk_stride_h, a->dv_stride_b, a->dv_stride_s, a->dv_stride_h};
   for (int i = 0; i < 24; ++i) {
-    if (strides[i] < 0) return EA_EUNSUPPORTED;
+    if (strides[i] < 0 || strides[i] > kMaxExtentBytes) return EA_EUNSUPPORTED;
     if ((strides[i] * 2) % 16 != 0) return EA_EUNSUPPORTED;
   }
   for (int i = 0; i < 10; ++i) {
@@ -238,11 +282,22 @@ int validate_bwd(const ea_attn_bwd_args* a, bool* empty) {
   if (a->lse_stride_b < 0 || a->lse_stride_h < 0 || a->delta_stride_b < 0 || a->delta_stride_h < 0)
     return EA_EUNSUPPORTED;
   const int64_t lim = (int64_t)1 << 31;
-  if (N >= lim / 2 || B * H >= lim) return EA_EUNSUPPORTED;
-  if ((N + 127) / 128 * B * H >= lim / 2) return EA_EUNSUPPORTED;
+  int64_t bh = 0;
+  if (N >= lim / 2 || __builtin_mul_overflow(B, H, &bh) || bh >= lim) return EA_EUNSUPPORTED;
+  if ((N + 127) / 128 * bh >= lim / 2) return EA_EUNSUPPORTED;
   for (int i = 0; i < 8; ++i) {
     if (strides[3 * i + 1] >= lim || strides[3 * i + 1] * N >= lim) return EA_EUNSUPPORTED;
     if (strides[3 * i + 1] * 64 * 2 >= lim) return EA_EUNSUPPORTED;
+  }
+  {
+    int64_t bytes = 0;
+    const int64_t heads[8] = {H, Hk, Hk, H, H, H, Hk, Hk};
+    for (int i = 0; i < 8; ++i)
+      if (!extent_of(B, N, heads[i], D, strides[3 * i], strides[3 * i + 1], strides[3 * i + 2], 2, &bytes))
+        return EA_EUNSUPPORTED;
+    if (!rows_f32_fit(B, H, N, a->lse_stride_b, a->lse_stride_h) ||
+        !rows_f32_fit(B, H, N, a->delta_stride_b, a->delta_stride_h))
+      return EA_EUNSUPPORTED;
   }
   // outputs (dq, dk, dv, delta) overlap neither each other nor any input
   const Span in[6] = {span_of(a->q, B, N, H, D, a->q_stride_b, a->q_stride_s, a->q_stride_h, 2),
@@ -287,8 +342,8 @@ ea::BwdParams make_bwd_params(const ea_attn_bwd_args* a) {
   p.lse_sb = a->lse_stride_b; p.lse_sh = a->lse_stride_h;
   p.delta_sb = a->delta_stride_b; p.delta_sh = a->delta_stride_h;
   p.causal = a->causal ? 1 : 0;
-  p.wl = a->window_left;
-  p.wr = a->window_right;
+  p.wl = effective_window(a->window_left, a->seqlen);
+  p.wr = effective_window(a->window_right, a->seqlen);
   p.scale = a->softmax_scale;
   p.c_log2 = (float)((double)a->softmax_scale * 1.4426950408889634);
   return p;

@@ -154,6 +154,13 @@ def test_plan_tile_counts_causal_and_window():
     ("lse", FAKE + 3 * SIZE + 64, _lib.EA_EINVAL),  # lse inside o
     # an absurd row stride is refused before any product with it can wrap
     ("k_stride_s", 1 << 62, _lib.EA_EUNSUPPORTED),
+    # so are batch and head strides and LSE strides whose extents overflow
+    ("q_stride_b", 1 << 62, _lib.EA_EUNSUPPORTED),
+    ("v_stride_h", (1 << 62) + 8, _lib.EA_EUNSUPPORTED),
+    ("o_stride_b", (1 << 46) // 2 * 8, _lib.EA_EUNSUPPORTED),   # fits int64, extent past 2^47 bytes
+    ("lse_stride_b", 1 << 61, _lib.EA_EUNSUPPORTED),
+    ("lse_stride_h", 1 << 62, _lib.EA_EUNSUPPORTED),
+    ("batch", 1 << 40, _lib.EA_EUNSUPPORTED),
 ])
 def test_validation_errors(field, value, code):
     a = make()
@@ -320,6 +327,10 @@ BWD_SIZE = 2 * 300 * 3 * 128 * 4 + 4096   # make_bwd()'s spacing of the fake ten
     ("q_stride_s", 3 * 128 + 4, _lib.EA_EUNSUPPORTED),
     ("dk_stride_h", -128, _lib.EA_EUNSUPPORTED),
     ("v_stride_s", 1 << 62, _lib.EA_EUNSUPPORTED),
+    ("dq_stride_b", 1 << 62, _lib.EA_EUNSUPPORTED),
+    ("k_stride_h", (1 << 62) + 8, _lib.EA_EUNSUPPORTED),
+    ("delta_stride_b", 1 << 62, _lib.EA_EUNSUPPORTED),
+    ("nheads_q", 3 << 40, _lib.EA_EUNSUPPORTED),
 ])
 def test_bwd_validation_errors(field, value, code):
     # every failing check returns before a device is queried
@@ -334,3 +345,35 @@ def test_bwd_empty_problem_is_ok_without_pointers():
         for t in ("q", "k", "v", "o", "dout", "lse", "delta", "dq", "dk", "dv"):
             setattr(a, t, 0)
         assert _lib.lib().ea_attn_bwd(ctypes.byref(a), None) == _lib.EA_OK
+
+
+@pytest.mark.parametrize("causal", [0, 1])
+def test_window_bounds_past_the_sequence_plan_as_unbounded(causal):
+    # a window bound >= N reaches past every key: the plan (tile walk, grid,
+    # split) is that of -1, also at int32's largest value, where the row +
+    # bound sums would otherwise wrap
+    big = 2 ** 31 - 1
+    for N in (300, 4096):
+        st, ref = plan_status(make(B=1, N=N, H=2, causal=causal))
+        assert st == 0
+        for wl, wr in ((big, big), (big, -1), (-1, big), (N, N), (N, 0 if causal else N)):
+            st, info = plan_status(make(B=1, N=N, H=2, causal=causal, window_left=wl, window_right=wr))
+            assert st == 0, (wl, wr)
+            got = (info.grid, info.kv_tiles, info.masked_tiles, info.splits, info.workspace_bytes)
+            want = (ref.grid, ref.kv_tiles, ref.masked_tiles, ref.splits, ref.workspace_bytes)
+            assert got == want, (N, wl, wr, got, want)
+    # a bound just inside the sequence still bounds
+    st, info = plan_status(make(B=1, N=4096, H=2, causal=causal, window_left=4094, window_right=0))
+    assert st == 0 and info.kv_tiles < plan_status(make(B=1, N=4096, H=2))[1].kv_tiles
+
+
+def test_python_window_values_are_range_checked():
+    import torch
+    from exact_attention_04_amd.attention import make_args
+    x = torch.zeros(1, 8, 1, 64, dtype=torch.float16)
+    # past int32: the largest int32 (unbounded, as any bound >= N), never a wrapped value
+    a = make_args(x, x, x, x, None, window_size=(2 ** 40, 2 ** 33 + 5))
+    assert (a.window_left, a.window_right) == (2 ** 31 - 1, 2 ** 31 - 1)
+    for bad in ((-2, 0), (0, -(2 ** 32) + 5), (-(2 ** 40), -1)):
+        with pytest.raises(ValueError):
+            make_args(x, x, x, x, None, window_size=bad)
