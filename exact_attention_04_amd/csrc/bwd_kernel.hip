@@ -179,7 +179,7 @@ attn_bwd_dq_kernel(const BwdParams p) {
     float part = 0.f;
 #pragma unroll
     for (int st = 0; st < C::kSteps; ++st) part += dot8<IN>(df[st], of[st]);
-    delta = part + __shfl_xor(part, 32);
+    delta = pair_sum(part);
   }
   // P = exp2(s c - lse log2 e); rows past n (and rows that saw no key) give 0
   float lse2 = INFINITY;
@@ -651,12 +651,6 @@ hipError_t launch_bwd(const BwdParams& p, int in_dtype, int d, hipStream_t strea
   if (in_dtype == 2 && d == 64) return launch_bwd_t<In::BF16, 64>(p, stream);
   if (in_dtype == 2 && d == 128) return launch_bwd_t<In::BF16, 128>(p, stream);
   return hipErrorInvalidValue;
-}
-
-const char* bwd_kernel_names(int in_dtype, int d) {
-  static const char* names[2][2] = {{"attn_bwd<f16,d64>", "attn_bwd<f16,d128>"}, {"attn_bwd<bf16,d64>", "attn_bwd<bf16,d128>"}};
-  if (in_dtype < 1 || in_dtype > 2 || (d != 64 && d != 128)) return "none";
-  return names[in_dtype - 1][d == 128];
 }
 
 }  // namespace ea

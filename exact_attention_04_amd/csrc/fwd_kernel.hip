@@ -1,10 +1,11 @@
 // Exact attention forward for gfx950 (CDNA4): fused Q.K^T -> online softmax
 // -> P.V, one workgroup per (batch, head, query tile).
 //
-// The method ("FlashAttention", aiunderstanding.org, "Teknisk insikt"): load
-// small blocks of queries, keys and values on chip, compute partial outputs,
-// and rescale running sums as new blocks arrive, so the N x N score matrix is
-// never written to HBM and the whole attention is one kernel.
+// Method: "FlashAttention" (aiunderstanding.org), section "Teknisk insikt".
+// Each workgroup keeps its query rows' partial output, row maximum and row
+// sum on chip while it walks over the key/value blocks, so scores and
+// probabilities exist only in registers, one block at a time; HBM sees Q, K
+// and V read and O and the log-sum-exp written, nothing of size N x N.
 //
 // How it maps onto a CDNA4 compute unit:
 //   * A workgroup is 4 waves; each wave owns RB blocks of 32 query rows
@@ -43,8 +44,6 @@
 //     never loaded.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
-
-#include <algorithm>
 
 #include "fwd_kernel.h"
 #include "kernel_common.h"
@@ -420,31 +419,37 @@ attn_fwd_kernel(const FwdParams p) {
       }
     }
   };
-  // p = exp2(s c - m c) for a 32-key half of every row block, packed to 16
-  // bits; the row sum takes the unrounded fp32 p (the LSE needs it to fp32
-  // accuracy, which a sum of 16-bit p would miss by up to 2^-9).
-  auto exp_pack = [&](const f32x16 (&s)[RB], uint32_t (&pk)[RB][8]) {
+  // p = exp2(x), x = s c - m c, for a 32-key half of every row block, packed
+  // to 16 bits; the row sum takes the unrounded fp32 p (the LSE needs it to
+  // fp32 accuracy, which a sum of 16-bit p would miss by up to 2^-9), and
+  // x_top the largest x.
+  auto exp_pack = [&](const f32x16 (&s)[RB], uint32_t (&pk)[RB][8], float (&x_top)[RB]) {
 #pragma unroll
     for (int qb = 0; qb < RB; ++qb)
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
-        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][2 * r], cexp, neg_mc[qb]));
-        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][2 * r + 1], cexp, neg_mc[qb]));
+        const float x0 = __builtin_fmaf(s[qb][2 * r], cexp, neg_mc[qb]);
+        const float x1 = __builtin_fmaf(s[qb][2 * r + 1], cexp, neg_mc[qb]);
+        x_top[qb] = fmaxf(x_top[qb], fmaxf(x0, x1));
+        const float e0 = __builtin_amdgcn_exp2f(x0);
+        const float e1 = __builtin_amdgcn_exp2f(x1);
         l_part[qb] += e0;
         l_part[qb] += e1;
         pk[qb][r] = pack2<PIN>(e0, e1);
       }
   };
-  // The 16-bit rounding residual p - round16(p) of a half packed by exp_pack
-  // with the same reference, itself packed to 16 bits.
-  auto residual = [&](const f32x16 (&s)[RB], const uint32_t (&pk)[RB][8], uint32_t (&pr)[RB][8]) {
+  // The 16-bit rounding residual p - round16(p) of k-step j (keys
+  // 16 j .. 16 j + 15 of a half packed by exp_pack, with the same reference),
+  // itself packed to 16 bits.
+  auto residual = [&](const f32x16 (&s)[RB], const uint32_t (&pk)[RB][8], int j, uint32_t (&pr)[RB][4]) {
 #pragma unroll
     for (int qb = 0; qb < RB; ++qb)
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
+      for (int t = 0; t < 4; ++t) {
+        const int r = 4 * j + t;
         const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][2 * r], cexp, neg_mc[qb]));
         const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][2 * r + 1], cexp, neg_mc[qb]));
-        pr[qb][r] = pack2<PIN>(e0 - unpack_lo<PIN>(pk[qb][r]), e1 - unpack_hi<PIN>(pk[qb][r]));
+        pr[qb][t] = pack2<PIN>(e0 - unpack_lo<PIN>(pk[qb][r]), e1 - unpack_hi<PIN>(pk[qb][r]));
       }
   };
   // e4m3 P (P8): p * 2^kPShift for a 32-key half, rounded to nearest e4m3
@@ -521,7 +526,7 @@ attn_fwd_kernel(const FwdParams p) {
   // Each step is fenced (sched_barrier), so the compiler keeps this order
   // instead of grouping the MFMAs and the vector work apart (16-bit inputs).
   auto s_phase = [&](const unsigned char* kn, int hb, f32x16 (&sn)[RB], const f32x16 (&sc)[RB],
-                     uint32_t (&pk)[RB][8], auto&& hook) {
+                     uint32_t (&pk)[RB][8], float (&x_top)[RB], auto&& hook) {
     constexpr int kSteps = C::kQSteps;
     constexpr int kPre = kSteps < 4 ? kSteps : 4;      // K reads in flight
     constexpr int kPairsPerStep = 8 / kSteps;          // packed P pairs per step
@@ -545,8 +550,11 @@ attn_fwd_kernel(const FwdParams p) {
 #pragma unroll
         for (int u = 0; u < kPairsPerStep; ++u) {
           const int r = st * kPairsPerStep + u;
-          const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[qb][2 * r], cexp, neg_mc[qb]));
-          const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[qb][2 * r + 1], cexp, neg_mc[qb]));
+          const float x0 = __builtin_fmaf(sc[qb][2 * r], cexp, neg_mc[qb]);
+          const float x1 = __builtin_fmaf(sc[qb][2 * r + 1], cexp, neg_mc[qb]);
+          x_top[qb] = fmaxf(x_top[qb], fmaxf(x0, x1));
+          const float e0 = __builtin_amdgcn_exp2f(x0);
+          const float e1 = __builtin_amdgcn_exp2f(x1);
           l_part[qb] += e0;
           l_part[qb] += e1;
           pk[qb][r] = pack2<PIN>(e0, e1);
@@ -577,14 +585,21 @@ attn_fwd_kernel(const FwdParams p) {
   // MFMAs of the same half of the next tile (`sn`, from the K slot `kn`),
   // then O += P V over the current V slot `vl`.  Issue is in order per wave,
   // so this interleave is what lets the vector ALU and the matrix core work
-  // at the same time.  `masked`: tile kt crosses a mask edge or the sequence
-  // end.  On such tiles the 16-bit rounding of p can matter: when the half
-  // carries a large share of a row's weight (the first keys of a row, or a
-  // row whose weight concentrates on its latest keys), its rounding errors do
-  // not average out against the rest of the row.  If for some row of the
-  // wave the half adds more than 1/16 of the row's sum so far, the rounding
-  // residual p - round16(p) goes through a second P.V pass; otherwise its
-  // contribution to the error is below 2^-13 of max |v|.
+  // at the same time.
+  // Rounding of P.  A 16-bit p carries a relative error of up to 2^-8 (bf16)
+  // or 2^-11 (fp16).  Spread over many keys these errors average out; they do
+  // not where a few keys hold a large share of a row's weight: a row's first
+  // keys, or a peaked row whose dominant keys may sit anywhere in its range.
+  // So a half holding a key whose p exceeds 1/kPeak of its row's running sum
+  // (kPeak 8 for bf16 P, 4 for fp16; in the exp2-argument domain,
+  // x > log2(l) - log2(kPeak)) also multiplies the rounding residual
+  // p - round16(p), itself in 16 bits: P is effectively 16+16 bits there.
+  // Every other key carries less than 1/kPeak of its row's final weight,
+  // which caps its own rounding error at 2^-11 |v| (bf16) or 2^-13 |v|
+  // (fp16).  The largest x of the half comes from the softmax steps (one max
+  // per pair of scores); the test is wave-uniform (a ballot over the wave's
+  // rows) and its branch follows the main P.V MFMAs, by which time its
+  // operands are ready.
   constexpr int kSMfma = RB * C::kQSteps;            // S MFMAs per half (all row blocks)
   constexpr int kExpValu = RB * 56;                  // softmax VALU per half (all row blocks)
   // `hook(st)` runs after the S MFMA of k-step st; the first unit of an
@@ -593,12 +608,12 @@ attn_fwd_kernel(const FwdParams p) {
   // would stall the waves that leave a barrier together on the address unit.
   // (The scheduler cannot move those loads past LDS reads by itself: they
   // write LDS.)
-  auto unit = [&](auto next_tag, auto dma_tag, f32x16 (&sc)[RB], bool masked, int hb, const unsigned char* vl,
-                  const unsigned char* kn, f32x16 (&sn)[RB], auto&& hook) {
+  auto unit = [&](auto next_tag, f32x16 (&sc)[RB], int hb, const unsigned char* vl, const unsigned char* kn,
+                  f32x16 (&sn)[RB], auto&& hook) {
     uint32_t pk[RB][8];
-    float l_before[RB];
+    float x_top[RB];
 #pragma unroll
-    for (int qb = 0; qb < RB; ++qb) l_before[qb] = l_part[qb];
+    for (int qb = 0; qb < RB; ++qb) x_top[qb] = -INFINITY;
     if constexpr (decltype(next_tag)::value) {
       // raised priority while the S MFMAs and the softmax interleave: when
       // both waves of a SIMD have work, the one feeding the matrix core from
@@ -606,7 +621,7 @@ attn_fwd_kernel(const FwdParams p) {
       __builtin_amdgcn_s_setprio(1);
       if constexpr (C::kFp8) {
         s_half(kn, hb, sn, hook);
-        exp_pack(sc, pk);
+        exp_pack(sc, pk, x_top);
 #pragma unroll
         for (int i = 0; i < kSMfma; ++i) {
           if (i % (4 * RB) == 0) __builtin_amdgcn_sched_group_barrier(0x100, 2 * C::kQSteps, 0);  // K reads
@@ -614,22 +629,27 @@ attn_fwd_kernel(const FwdParams p) {
           __builtin_amdgcn_sched_group_barrier(0x002, kExpValu / kSMfma, 0);                  // softmax VALU
         }
       } else {
-        s_phase(kn, hb, sn, sc, pk, hook);
+        s_phase(kn, hb, sn, sc, pk, x_top, hook);
       }
     } else {
-      exp_pack(sc, pk);
+      exp_pack(sc, pk, x_top);
     }
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(0);
-    bool heavy = false;
+    constexpr float kLgPeak = (PIN == In::F16) ? 2.f : 3.f;   // log2(kPeak)
+    bool peak = false;
 #pragma unroll
-    for (int qb = 0; qb < RB; ++qb) heavy = heavy || ((l_part[qb] - l_before[qb]) * 16.f > l_part[qb]);
-    if (masked && __builtin_amdgcn_ballot_w64(heavy) != 0) {
-      uint32_t pr[RB][8];
-      residual(sc, pk, pr);
-      pv_half<PIN, D, RB>(acc, pr, vl, va, hb);
-    }
+    for (int qb = 0; qb < RB; ++qb)
+      peak = peak || x_top[qb] > __builtin_amdgcn_logf(pair_sum(l_part[qb])) - kLgPeak;
     pv_half<PIN, D, RB>(acc, pk, vl, va, hb);
+    if (__builtin_amdgcn_ballot_w64(peak) != 0) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        uint32_t pr[RB][4];
+        residual(sc, pk, j, pr);
+        pv_kstep<PIN, D, RB>(acc, pr, vl, va, hb, j);
+      }
+    }
     __builtin_amdgcn_sched_barrier(0);
   };
   // e4m3 P.V (P8): a unit only computes the softmax of the current half
@@ -680,7 +700,7 @@ attn_fwd_kernel(const FwdParams p) {
   // the two units, and ends with a barrier once its DMA has landed.
   f32x16 s_a[RB], s_b[RB];
   auto iter = [&](int kt, const unsigned char* kread, const unsigned char* vread, unsigned char* kwrite,
-                  unsigned char* vwrite, bool& m_cur) {
+                  unsigned char* vwrite) __attribute__((always_inline)) {
     if (wave_needs_ref()) fold_max(s_a, s_b);
     const bool m_next = tile_masked(kt + 1);
     f32x16 n_a[RB], n_b[RB];
@@ -707,9 +727,9 @@ attn_fwd_kernel(const FwdParams p) {
       if (m_next) apply_mask(n_b, (kt + 1) * kBN, 1);
       tile_pv8(s_a, s_b, pa, pb, l_tile, vread);
     } else {
-      unit(BoolTag<true>{}, IntTag<kDmaK + kDmaV>{}, s_a, m_cur, 0, vread, kread, n_a, dma_hook);
+      unit(BoolTag<true>{}, s_a, 0, vread, kread, n_a, dma_hook);
       if (m_next) apply_mask(n_a, (kt + 1) * kBN, 0);
-      unit(BoolTag<true>{}, IntTag<0>{}, s_b, m_cur, 1, vread, kread, n_b, [](int) {});
+      unit(BoolTag<true>{}, s_b, 1, vread, kread, n_b, [](int) {});
       if (m_next) apply_mask(n_b, (kt + 1) * kBN, 1);
     }
 #pragma unroll
@@ -717,12 +737,11 @@ attn_fwd_kernel(const FwdParams p) {
       s_a[qb] = n_a[qb];
       s_b[qb] = n_b[qb];
     }
-    m_cur = m_next;
     store_v_fp8(vwrite);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
-  auto key_loop = [&]() {
+  auto key_loop = [&]() __attribute__((always_inline)) {
     if (kt_begin >= kt_end) return;
     issue_k(kt_begin, kbuf0);
     issue_v(kt_begin, vbuf0);
@@ -732,8 +751,7 @@ attn_fwd_kernel(const FwdParams p) {
     __syncthreads();
     s_half(kbuf0, 0, s_a, [](int) {});
     s_half(kbuf0, 1, s_b, [](int) {});
-    bool m_cur = tile_masked(kt_begin);
-    if (m_cur) {
+    if (tile_masked(kt_begin)) {
       apply_mask(s_a, kt_begin * kBN, 0);
       apply_mask(s_b, kt_begin * kBN, 1);
     }
@@ -742,12 +760,12 @@ attn_fwd_kernel(const FwdParams p) {
     const int with_next = kt_end - 1 - kt_begin;
     int kt = kt_begin;
     for (int j = 0; j < with_next / 2; ++j, kt += 2) {
-      iter(kt, kbuf1, vbuf0, kbuf0, vbuf1, m_cur);
-      iter(kt + 1, kbuf0, vbuf1, kbuf1, vbuf0, m_cur);
+      iter(kt, kbuf1, vbuf0, kbuf0, vbuf1);
+      iter(kt + 1, kbuf0, vbuf1, kbuf1, vbuf0);
     }
     const bool odd = (with_next & 1) != 0;
     if (odd) {
-      iter(kt, kbuf1, vbuf0, kbuf0, vbuf1, m_cur);
+      iter(kt, kbuf1, vbuf0, kbuf0, vbuf1);
       ++kt;
     }
     // last tile: softmax and P.V only
@@ -762,8 +780,8 @@ attn_fwd_kernel(const FwdParams p) {
       unit8(BoolTag<false>{}, s_b, 1, kbuf0, s_b, pb, [](int) {});
       tile_pv8(s_a, s_b, pa, pb, l_tile, vlast);
     } else {
-      unit(BoolTag<false>{}, IntTag<0>{}, s_a, m_cur, 0, vlast, kbuf0, s_a, [](int) {});
-      unit(BoolTag<false>{}, IntTag<0>{}, s_b, m_cur, 1, vlast, kbuf0, s_b, [](int) {});
+      unit(BoolTag<false>{}, s_a, 0, vlast, kbuf0, s_a, [](int) {});
+      unit(BoolTag<false>{}, s_b, 1, vlast, kbuf0, s_b, [](int) {});
     }
     __syncthreads();   // the slots are reused by a second pass
   };
@@ -798,7 +816,7 @@ attn_fwd_kernel(const FwdParams p) {
     bool bad = false;
 #pragma unroll
     for (int qb = 0; qb < RB; ++qb) {
-      float t = l_part[qb] + __shfl_xor(l_part[qb], 32);
+      float t = pair_sum(l_part[qb]);
 #pragma unroll
       for (int c = 0; c < C::kDBlocks; ++c)
 #pragma unroll
@@ -825,7 +843,7 @@ attn_fwd_kernel(const FwdParams p) {
   // ---- epilogue: O = O_acc / l (* v descale), LSE = ln(2) * (m c + log2 l)
 #pragma unroll
   for (int qb = 0; qb < RB; ++qb) {
-    const float l_row = l_part[qb] + __shfl_xor(l_part[qb], 32);
+    const float l_row = pair_sum(l_part[qb]);
     if (qrow[qb] < n && p.splits > 1) {
       // partial result of this key chunk: normalised O in fp32 and its LSE,
       // merged by attn_fwd_combine
@@ -931,42 +949,6 @@ static hipError_t launch_t(const FwdParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Kernel configurations: 128 query rows per workgroup (4 waves x 32 rows,
-// two workgroups per CU), 64 keys per K/V tile; configuration 1 (fp8 inputs
-// only) runs P.V on the e4m3 matrix instruction.
-int tile_bm(int /*cfg*/) { return 128; }
-
-// Key split.  Measured on gfx950: a split pays for its merge kernel (a few
-// microseconds) only where the query tiles' work is unbalanced (causal or
-// windowed masks), by cutting the heaviest tiles; on balanced launches it
-// costs.  So: no split when the items fill two workgroups per CU on the 256
-// CUs, or when the heaviest tile sees fewer than 1.5x the average key tiles;
-// otherwise enough chunks to bring the heaviest tile to about the average,
-// within the GPU's two-per-CU capacity, with at least two key tiles per chunk
-// and at most 16 chunks.
-int choose_splits(int64_t items, int max_kv_tiles, int64_t total_kv_tiles) {
-  constexpr int64_t kResident = 2 * 256;
-  if (items <= 0 || items >= kResident || total_kv_tiles <= 0) return 1;
-  if (2 * (int64_t)max_kv_tiles * items < 3 * total_kv_tiles) return 1;   // balanced
-  int64_t s = ((int64_t)max_kv_tiles * items + total_kv_tiles - 1) / total_kv_tiles;
-  s = std::min<int64_t>(s, (kResident + items - 1) / items);
-  s = std::min<int64_t>(s, max_kv_tiles / 2);
-  s = std::min<int64_t>(s, 16);
-  return (int)std::max<int64_t>(s, 1);
-}
-
-int64_t split_workspace_bytes(int splits, int64_t batch_heads, int64_t n, int d) {
-  return splits > 1 ? (int64_t)splits * batch_heads * n * (d + 1) * 4 : 0;
-}
-int tile_waves(int /*cfg*/) { return 4; }
-int tile_bn() { return kBN; }
-
-int lds_bytes(int in_dtype, int d, int cfg) {
-  const bool fp8 = in_dtype == 3;
-  const int kin = fp8 ? 1 : 2;
-  return 2 * (kBN * d * kin + kBN * d * (cfg == 1 ? 1 : 2));
-}
-
 hipError_t launch_fwd(const FwdParams& p, int in_dtype, int d, int cfg, hipStream_t stream) {
   // in_dtype: 1 = f16, 2 = bf16, 3 = fp8 e4m3 (validated by the caller)
   if (cfg == 1) {
@@ -980,15 +962,6 @@ hipError_t launch_fwd(const FwdParams& p, int in_dtype, int d, int cfg, hipStrea
   if (in_dtype == 2 && d == 128) return launch_t<In::BF16, 128, 4, 1>(p, stream);
   if (in_dtype == 3 && d == 128) return launch_t<In::FP8, 128, 4, 1>(p, stream);
   return hipErrorInvalidValue;
-}
-
-const char* kernel_name(int in_dtype, int d, int cfg) {
-  static const char* names[3][2] = {{"attn_fwd<f16,d64,bm128,bn64>", "attn_fwd<f16,d128,bm128,bn64>"},
-                                    {"attn_fwd<bf16,d64,bm128,bn64>", "attn_fwd<bf16,d128,bm128,bn64>"},
-                                    {"none", "attn_fwd<fp8,d128,bm128,bn64>"}};
-  if (cfg == 1) return (in_dtype == 3 && d == 128) ? "attn_fwd<fp8,pv8,d128,bm128,bn64>" : "none";
-  if (in_dtype < 1 || in_dtype > 3 || (d != 64 && d != 128)) return "none";
-  return names[in_dtype - 1][d == 128];
 }
 
 }  // namespace ea

@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "tiles.h"
+
 namespace ea {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -20,7 +22,6 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
-constexpr int kBN = 64;            // keys per K/V tile
 constexpr float kLn2 = 0.6931471805599453f;
 
 enum class In { F16, BF16, FP8 };
@@ -132,9 +133,27 @@ __device__ __forceinline__ uint4 load_16b(const void* base, int bytes, uint32_t 
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(buffer_rsrc(base, bytes), voff, 0, 0));
 }
 
-// Max over the two lanes l, l^32 of a wave (they hold the two key halves of
-// one query row).
-__device__ __forceinline__ float pair_max(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
+// The values of lanes l and l ^ 32 of a wave (the two key halves of one query
+// row), both in every lane: one v_permlane32_swap exchanges the upper 32 lanes
+// of one copy with the lower 32 lanes of the other, so the two results hold
+// {lane l, lane l ^ 32} in some order (no LDS round trip).
+struct LanePair {
+  float a, b;
+};
+__device__ __forceinline__ LanePair lane_pair(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return {__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1])};
+}
+// Sum and max over the two lanes of a query row.
+__device__ __forceinline__ float pair_sum(float x) {
+  const LanePair p = lane_pair(x);
+  return p.a + p.b;
+}
+__device__ __forceinline__ float pair_max(float x) {
+  const LanePair p = lane_pair(x);
+  return fmaxf(p.a, p.b);
+}
 
 // Visible-key range of query rows [q0, q0+qrows) and the mask classification
 // of a block of rows x keys.  Key j is visible from query i iff j < n,
@@ -170,15 +189,39 @@ __device__ __forceinline__ bool block_none_visible(int r0, int r1, int k0, int k
   return false;
 }
 
+// One 16-key k-step j of the P.V product below (pv_half): 4 packed P pairs
+// per row block.
+template <In PIN, int D, int RB>
+__device__ __forceinline__ void pv_kstep(f32x16 (&acc)[RB][D / 32], const uint32_t (&pk)[RB][4],
+                                         const unsigned char* vl, const uint32_t (&va)[2][D / 32], int hb, int j) {
+  // the fragment reads of the step are issued together, ahead of its MFMAs,
+  // so their latency is paid once per step rather than per MFMA
+  const unsigned char* base = vl + (32 * hb + 16 * j) * (2 * D);
+  uint4 aop[D / 32];
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c) {
+    const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + va[0][c]));
+    const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + va[1][c]));
+    const uint2 w0 = __builtin_bit_cast(uint2, t0);
+    const uint2 w1 = __builtin_bit_cast(uint2, t1);
+    aop[c] = make_uint4(w0.x, w0.y, w1.x, w1.y);
+  }
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+    for (int qb = 0; qb < RB; ++qb)
+      acc[qb][c] = mfma_16bit<PIN>(aop[c], make_uint4(pk[qb][0], pk[qb][1], pk[qb][2], pk[qb][3]), acc[qb][c]);
+}
+
 // O^T += V^T P^T for both row blocks over the 32 keys [32 hb, 32 hb + 32) of a
-// staged tile.  P^T (16-bit, B operand) is in the layout the S^T accumulator
-// left it: lane l holds query l%32 and, for k-step j0 in {0, 2}, keys
-// 32 hb + 8 j0 + {4 half + t, 8 + 4 half + t}, t < 4 (packed pairs
-// pk[2 j0 .. 2 j0 + 3]).  The matching V^T fragment (A operand: row d = l%32
-// of a 32-column block, the same 8 keys) is gathered with two transposing LDS
-// reads: within each 16-lane group, source lane sl points at key
-// base + sl/4, columns 4 (sl%4) .. +3, and lane i receives column i of the 4
-// consecutive keys.  Each fragment feeds both row blocks.
+// staged tile, as two k-steps of 16 keys (pv_kstep, j = 0, 1).  P^T (16-bit,
+// B operand) is in the layout the S^T accumulator left it: lane l holds query
+// l%32 and, for k-step j, keys 32 hb + 16 j + {4 half + t, 8 + 4 half + t},
+// t < 4 (packed pairs pk[4 j .. 4 j + 3]).  The matching V^T fragment (A
+// operand: row d = l%32 of a 32-column block, the same 8 keys) is gathered
+// with two transposing LDS reads: within each 16-lane group, source lane sl
+// points at key base + sl/4, columns 4 (sl%4) .. +3, and lane i receives
+// column i of the 4 consecutive keys.  Each fragment feeds both row blocks.
 //
 // `va[r8][c]` is this lane's byte offset, within a V tile, of its read for
 // key row 4 (g/2) + sl/4 + 8 r8 and column block c; moving by 16 or 32 key
@@ -187,28 +230,14 @@ __device__ __forceinline__ bool block_none_visible(int r0, int r1, int k0, int k
 template <In PIN, int D, int RB>
 __device__ __forceinline__ void pv_half(f32x16 (&acc)[RB][D / 32], const uint32_t (&pk)[RB][8],
                                         const unsigned char* vl, const uint32_t (&va)[2][D / 32], int hb) {
-  // the fragment reads of each 8-key step are issued together, ahead of its
-  // MFMAs, so their latency is paid once per step rather than per MFMA
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const unsigned char* base = vl + (32 * hb + 16 * j) * (2 * D);
-    uint4 aop[D / 32];
-#pragma unroll
-    for (int c = 0; c < D / 32; ++c) {
-      const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + va[0][c]));
-      const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + va[1][c]));
-      const uint2 w0 = __builtin_bit_cast(uint2, t0);
-      const uint2 w1 = __builtin_bit_cast(uint2, t1);
-      aop[c] = make_uint4(w0.x, w0.y, w1.x, w1.y);
-    }
-    uint4 bop[RB];
+    uint32_t pj[RB][4];
 #pragma unroll
     for (int qb = 0; qb < RB; ++qb)
-      bop[qb] = make_uint4(pk[qb][4 * j], pk[qb][4 * j + 1], pk[qb][4 * j + 2], pk[qb][4 * j + 3]);
 #pragma unroll
-    for (int c = 0; c < D / 32; ++c)
-#pragma unroll
-      for (int qb = 0; qb < RB; ++qb) acc[qb][c] = mfma_16bit<PIN>(aop[c], bop[qb], acc[qb][c]);
+      for (int t = 0; t < 4; ++t) pj[qb][t] = pk[qb][4 * j + t];
+    pv_kstep<PIN, D, RB>(acc, pj, vl, va, hb, j);
   }
 }
 

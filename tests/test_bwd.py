@@ -50,9 +50,23 @@ def to_bhsd(x, layout):
     return x if layout == "bhsd" else np.swapaxes(x, 1, 2)
 
 
+def head_bounds(q, k, v, do, o, scale, causal, window, dtype, p=None):
+    """Elementwise error bounds of one query head's contributions, all float64
+    [N, D] arrays: (dq bound, this head's share of the dk and dv bounds, the
+    delta bound)."""
+    u = U[dtype]
+    if p is None:
+        p = oracle.attention_probs_head(q, k, scale, causal, window[0], window[1])
+    dp = do @ v.T
+    dsum = np.sum(np.abs(do * o), axis=1)
+    d_exact = np.sum(do * (p @ v), axis=1)
+    e = p * (u * dsum)[:, None] + u * np.abs(p * (dp - d_exact[:, None]))
+    return (2 * scale * (e @ np.abs(k)), 2 * scale * (e.T @ np.abs(q)), 2 * u * (p.T @ np.abs(do)),
+            1e-5 * (1 + dsum))
+
+
 def bounds(qf, kf, vf, dof, o16f, scale, causal, window, layout, dtype):
     """Elementwise error bounds for dq, dk, dv (input layout) and delta."""
-    u = U[dtype]
     q, k, v, do, o = (to_bhsd(x, layout) for x in (qf, kf, vf, dof, o16f))
     B, H, N, D = q.shape
     Hk = k.shape[1]
@@ -60,20 +74,14 @@ def bounds(qf, kf, vf, dof, o16f, scale, causal, window, layout, dtype):
     bk = np.zeros_like(k)
     bv = np.zeros_like(v)
     bd = np.zeros((B, H, N))
-    vis = oracle.visible(np.arange(N)[:, None], np.arange(N)[None, :], N, causal, window[0], window[1])
     for b in range(B):
         for h in range(H):
             g = oracle.kv_head_of(h, H, Hk)
-            p = oracle.attention_probs_head(q[b, h], k[b, g], scale, causal, window[0], window[1])
-            p = np.where(vis, p, 0.0)
-            dp = do[b, h] @ v[b, g].T
-            dsum = np.sum(np.abs(do[b, h] * o[b, h]), axis=1)
-            d_exact = np.sum(do[b, h] * (p @ v[b, g]), axis=1)
-            e = p * (u * dsum)[:, None] + u * np.abs(p * (dp - d_exact[:, None]))
-            bv[b, g] += 2 * u * (p.T @ np.abs(do[b, h]))
-            bk[b, g] += 2 * scale * (e.T @ np.abs(q[b, h]))
-            bq[b, h] = 2 * scale * (e @ np.abs(k[b, g]))
-            bd[b, h] = 1e-5 * (1 + dsum)
+            hq, hk, hv, hd = head_bounds(q[b, h], k[b, g], v[b, g], do[b, h], o[b, h], scale, causal, window, dtype)
+            bq[b, h] = hq
+            bk[b, g] += hk
+            bv[b, g] += hv
+            bd[b, h] = hd
     back = (lambda x: x) if layout == "bhsd" else (lambda x: np.swapaxes(x, 1, 2))
     return back(bq) + 1e-6, back(bk) + 1e-6, back(bv) + 1e-6, bd
 
@@ -209,3 +217,58 @@ def test_bwd_empty_and_errors():
             attention_backward(q, q, q, q, q, lse, **kw)
     with pytest.raises(ValueError):
         attention_backward(q, q, q, q, q, lse.to(torch.bfloat16))
+
+
+@pytest.mark.parametrize("name", ["sdpa_b4h32n4096d128_bf16_causal", "gqa_b4h32kv8n4096d128_bf16_causal"])
+def test_bwd_workload_full_size(name):
+    # The timed backward pipeline at full size (the GPU forward's O and LSE,
+    # then the backward, B=4 H=32 N=4096 d=128 bf16 causal, BSHD), compared
+    # element by element on whole sampled heads: the first and last (batch,
+    # K/V head) and two random ones; with shared K/V heads every query head
+    # of those groups, whose dK and dV sum over the group.
+    from exact_attention_04_amd.workloads import WORKLOADS, make_inputs
+    w = WORKLOADS[name]
+    inp = make_inputs(w)
+    td = torch_dtype(w.dtype)
+    rng = np.random.default_rng(w.seed + 7)
+    do = torch.from_numpy(rng.standard_normal(tuple(inp.q.shape)).astype(np.float32)).to(td)
+    scale, causal, window = w.softmax_scale, w.causal, (w.window_left, w.window_right)
+    q, k, v, dog = (t.cuda() for t in (inp.q, inp.k, inp.v, do))
+    o, lse = attention(q, k, v, causal=causal, window_size=window, softmax_scale=scale, layout=w.layout)
+    dq, dk, dv, delta = attention_backward(q, k, v, o, dog, lse, causal=causal, window_size=window,
+                                           softmax_scale=scale, layout=w.layout)
+    torch.cuda.synchronize()
+    assert all(bool(torch.isfinite(t.float()).all()) for t in (dq, dk, dv, delta))
+    group = w.heads // w.kv_heads
+    picks = [(0, 0), (w.batch - 1, w.kv_heads - 1)]
+    picks += [(int(rng.integers(w.batch)), int(rng.integers(w.kv_heads))) for _ in range(2)]
+    for b, g in picks:
+        kf, vf = f64(inp.k[b, :, g]), f64(inp.v[b, :, g])
+        dk_ref, dv_ref = np.zeros_like(kf), np.zeros_like(vf)
+        bk, bv = np.zeros_like(kf), np.zeros_like(vf)
+        for h in range(g * group, (g + 1) * group):
+            qf, dof, o16 = f64(inp.q[b, :, h]), f64(do[b, :, h]), f64(o[b, :, h])
+            dq_r, dk_r, dv_r, _ = oracle.attention_backward_head(qf, kf, vf, dof, scale, causal, *window)
+            p = oracle.attention_probs_head(qf, kf, scale, causal, *window)
+            hq, hk, hv, hd = head_bounds(qf, kf, vf, dof, o16, scale, causal, window, w.dtype, p=p)
+            # the forward's own O error enters D (bounded by the forward's
+            # tolerance, 2e-3 plus one output ulp), as in the pipeline tests
+            o_exact, _ = oracle.attention_head(qf, kf, vf, scale, causal, *window)
+            ex = np.sum(np.abs(dof) * (2e-3 + ulp16(o_exact, w.dtype)), axis=1)
+            e = 2 * p * ex[:, None]
+            hq = hq + scale * (e @ np.abs(kf)) + 1e-6
+            hk = hk + scale * (e.T @ np.abs(qf))
+            dk_ref += dk_r
+            dv_ref += dv_r
+            bk += hk
+            bv += hv
+            err = np.abs(f64(dq[b, :, h]) - dq_r)
+            worst = float((err - hq - ulp16(dq_r, w.dtype)).max())
+            assert worst <= 0, f"{name} dq (b={b}, h={h}) exceeds its bound by {worst:.3g}"
+            d_exact = np.sum(dof * o16, axis=1)
+            assert (np.abs(f64(delta[b, h]) - d_exact) <= hd).all(), f"{name} delta (b={b}, h={h})"
+        for nm, got, ref, bnd in (("dk", dk[b, :, g], dk_ref, bk + 1e-6), ("dv", dv[b, :, g], dv_ref, bv + 1e-6)):
+            err = np.abs(f64(got) - ref)
+            worst = float((err - bnd - ulp16(ref, w.dtype)).max())
+            assert worst <= 0, f"{name} {nm} (b={b}, K/V head {g}) exceeds its bound by {worst:.3g}"
+        print(name, (b, g), "ok")

@@ -211,3 +211,24 @@ def test_wrapper_refuses_mismatched_output_buffers():
     # q = k = 0: every weight is equal, so O is the mean of V (all zero) and LSE = ln 64
     assert torch.equal(o, torch.zeros_like(o))
     assert torch.allclose(lse, torch.full_like(lse, float(np.log(64.0))), atol=1e-5)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_window_bounds_past_the_sequence_mean_no_bound(causal):
+    # bounds >= N, up to int32's largest value (where the row + bound sums
+    # would wrap) and Python ints past int32, give the unbounded result
+    # bitwise, in the forward and in the backward
+    from exact_attention_04_amd import attention_backward
+    n = 300
+    q, k, v = _gpu(small_case(1, 2, n, 64, "bf16", "bshd", 8))
+    do = torch.randn_like(q.float()).to(q.dtype)
+    o_ref, l_ref = attention(q, k, v, causal=causal)
+    g_ref = attention_backward(q, k, v, o_ref, do, l_ref, causal=causal)
+    big = 2 ** 31 - 1
+    for win in [(big, big), (big, -1), (-1, big), (n, n), (2 ** 40, 2 ** 33)]:
+        o, l = attention(q, k, v, causal=causal, window_size=win)
+        g = attention_backward(q, k, v, o_ref, do, l_ref, causal=causal, window_size=win)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref) and torch.equal(l, l_ref), win
+        for a, b in zip(g, g_ref):
+            assert torch.equal(a, b), win
