@@ -13,12 +13,13 @@ import threading
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libea_attn.so")
 
-EA_OK, EA_EINVAL, EA_EUNSUPPORTED, EA_EDEVICE, EA_EHIP = 0, 1, 2, 3, 4
+EA_OK, EA_EINVAL, EA_EUNSUPPORTED, EA_EDEVICE, EA_EHIP, EA_ESCRATCH = 0, 1, 2, 3, 4, 5
 EA_F16, EA_BF16, EA_FP8_E4M3, EA_F32 = 1, 2, 3, 4
-EA_ABI_VERSION = 3
+EA_ABI_VERSION = 4
 
 # Every symbol the header declares.
-EXPORTS = ("ea_attn_fwd", "ea_attn_bwd", "ea_attn_plan", "ea_status_string", "ea_last_hip_error", "ea_abi_version")
+EXPORTS = ("ea_attn_fwd", "ea_attn_fwd_noalloc", "ea_attn_bwd", "ea_attn_plan", "ea_status_string",
+           "ea_last_hip_error", "ea_abi_version")
 
 
 class AttnArgs(ctypes.Structure):
@@ -117,6 +118,8 @@ def lib() -> ctypes.CDLL:
             h = ctypes.CDLL(LIB_PATH)
             h.ea_attn_fwd.argtypes = [ctypes.POINTER(AttnArgs), ctypes.c_void_p]
             h.ea_attn_fwd.restype = ctypes.c_int
+            h.ea_attn_fwd_noalloc.argtypes = [ctypes.POINTER(AttnArgs), ctypes.c_void_p]
+            h.ea_attn_fwd_noalloc.restype = ctypes.c_int
             h.ea_attn_bwd.argtypes = [ctypes.POINTER(BwdArgs), ctypes.c_void_p]
             h.ea_attn_bwd.restype = ctypes.c_int
             h.ea_attn_plan.argtypes = [ctypes.POINTER(AttnArgs), ctypes.POINTER(PlanInfo)]
@@ -150,19 +153,24 @@ class AttnError(RuntimeError):
 
 
 class AttnArgumentError(AttnError, ValueError):
-    """EA_EINVAL or EA_EUNSUPPORTED."""
+    """EA_EINVAL, EA_EUNSUPPORTED or EA_ESCRATCH."""
 
 
 def check(code: int) -> None:
     if code == EA_OK:
         return
-    if code in (EA_EINVAL, EA_EUNSUPPORTED):
+    if code in (EA_EINVAL, EA_EUNSUPPORTED, EA_ESCRATCH):
         raise AttnArgumentError(code)
     raise AttnError(code, lib().ea_last_hip_error() if code == EA_EHIP else 0)
 
 
 def fwd(args: AttnArgs, stream: int) -> int:
     return lib().ea_attn_fwd(ctypes.byref(args), ctypes.c_void_p(stream))
+
+
+def fwd_noalloc(args: AttnArgs, stream: int) -> int:
+    """The allocation-free forward (library scratch; args.workspace must be NULL)."""
+    return lib().ea_attn_fwd_noalloc(ctypes.byref(args), ctypes.c_void_p(stream))
 
 
 def bwd(args: BwdArgs, stream: int) -> int:

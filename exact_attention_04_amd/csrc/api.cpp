@@ -436,6 +436,42 @@ int ea_attn_fwd(const ea_attn_args* args, void* stream) {
   return EA_OK;
 }
 
+int ea_attn_fwd_noalloc(const ea_attn_args* args, void* stream) {
+  bool empty = false;
+  const int st = validate(args, &empty);
+  if (st != EA_OK || empty) return st;
+  if (args->struct_size >= kArgsV2Size && args->workspace != nullptr) return EA_EINVAL;
+  const int cfg = choose_cfg(args);
+  ea::FwdParams p = make_params(args, cfg);
+  int64_t need = 0;
+  const int splits = wanted_splits(p, cfg, (int)args->headdim, &need);
+  if (need > ea::kScratchBytes) return EA_ESCRATCH;   // before any device call
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    g_last_hip_error = (int)e;
+    return EA_EHIP;
+  }
+  if (!device_is_gfx950(dev)) return EA_EDEVICE;
+  if (splits > 1) {
+    void* scratch = nullptr;
+    e = ea::scratch_address(dev, &scratch);
+    if (e != hipSuccess) {
+      g_last_hip_error = (int)e;
+      return EA_EHIP;
+    }
+    p.splits = splits;
+    p.part_o = (float*)scratch;
+    p.part_lse = p.part_o + (int64_t)splits * p.batch * p.heads * p.n * args->headdim;
+  }
+  e = ea::launch_fwd(p, args->in_dtype, (int)args->headdim, cfg, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    g_last_hip_error = (int)e;
+    return EA_EHIP;
+  }
+  return EA_OK;
+}
+
 int ea_attn_bwd(const ea_attn_bwd_args* args, void* stream) {
   bool empty = false;
   const int st = validate_bwd(args, &empty);
@@ -490,6 +526,7 @@ const char* ea_status_string(int status) {
     case EA_EUNSUPPORTED: return "unsupported argument combination";
     case EA_EDEVICE: return "current device is not gfx950";
     case EA_EHIP: return "HIP runtime error";
+    case EA_ESCRATCH: return "the key split needs more scratch than the library's static buffer holds";
     default: return "unknown status";
   }
 }

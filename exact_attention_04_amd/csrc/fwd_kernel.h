@@ -37,6 +37,14 @@ int choose_splits(int64_t items, int max_kv_tiles, int64_t total_kv_tiles);
 // Workspace bytes for `splits` chunks (0 for one).
 int64_t split_workspace_bytes(int splits, int64_t batch_heads, int64_t n, int d);
 
+// The allocation-free entry point's scratch: a static device array of
+// kScratchBytes per GPU holding the key split's partial results (in place of
+// a caller's workspace).  scratch_address() returns its device address on
+// device `dev`, which must be the current device; the lookup runs once per
+// device and its result (or error) is kept.
+constexpr int64_t kScratchBytes = (int64_t)32 << 20;
+hipError_t scratch_address(int dev, void** ptr);
+
 // Kernel configurations, both 128 query rows per workgroup (4 waves of 32
 // rows, two waves per SIMD) and 64 keys per K/V tile: 0, P.V in 16 bits
 // (fp8 V widened exactly to bf16); 1 (fp8 inputs only), P and V in e4m3 on

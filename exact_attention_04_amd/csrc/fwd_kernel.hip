@@ -45,6 +45,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "fwd_kernel.h"
 #include "kernel_common.h"
 
@@ -932,6 +934,27 @@ __global__ void __launch_bounds__(256) attn_fwd_combine(const FwdParams p) {
   w.y = pack2<OUT>(o.z, o.w);
   *(uint2*)(og + d * 2) = w;
   if (p.lse != nullptr && d == 0) p.lse[(int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh + row] = lse;
+}
+
+// Scratch of the allocation-free entry point.  Each GPU the library runs on
+// holds its own copy for the life of the process; in host code `scratch` is
+// only a handle, so kernels receive the address hipGetSymbolAddress reports
+// for the current device.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+hipError_t scratch_address(int dev, void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::once_flag once[kMaxDevices];
+  static void* addr[kMaxDevices];
+  static hipError_t status[kMaxDevices];
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(once[dev], [dev] {
+    void* a = nullptr;
+    status[dev] = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    addr[dev] = status[dev] == hipSuccess ? a : nullptr;
+  });
+  *ptr = addr[dev];
+  return status[dev];
 }
 
 template <In IN, int D, int WAVES, int RB, bool P8 = false>

@@ -35,7 +35,7 @@
 extern "C" {
 #endif
 
-#define EA_ABI_VERSION 3u
+#define EA_ABI_VERSION 4u
 
 /* Status codes. */
 enum ea_status {
@@ -43,7 +43,9 @@ enum ea_status {
   EA_EINVAL = 1,        /* malformed arguments: see ea_attn_fwd */
   EA_EUNSUPPORTED = 2,  /* well-formed but outside what the kernels implement */
   EA_EDEVICE = 3,       /* the current device is not a gfx950 GPU */
-  EA_EHIP = 4           /* a HIP runtime call failed; see ea_last_hip_error */
+  EA_EHIP = 4,          /* a HIP runtime call failed; see ea_last_hip_error */
+  EA_ESCRATCH = 5       /* ea_attn_fwd_noalloc: the launch needs more scratch
+                           than the library's static buffer holds */
 };
 
 /* Element types. */
@@ -168,6 +170,26 @@ typedef struct ea_attn_plan_info {
  * scale, descale and window checks have passed (the pointers may be NULL).
  */
 int ea_attn_fwd(const ea_attn_args* args, void* stream);
+
+/*
+ * ea_attn_fwd_noalloc -- ea_attn_fwd for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  Same arguments, results and checks as ea_attn_fwd, but
+ * args->workspace must be NULL: a launch that splits its keys (the plan's
+ * splits > 1) keeps the partial results in a static device array of the
+ * library, 32 MiB per GPU, which each GPU the library runs on holds until the
+ * process ends.  Nothing is allocated, freed or copied by this call.
+ *   EA_EINVAL        as ea_attn_fwd, and a non-NULL workspace.
+ *   EA_ESCRATCH      the plan's workspace_bytes exceeds 32 MiB (checked
+ *                    before any device call; ea_attn_fwd with a caller
+ *                    workspace, or with none, runs such a problem).
+ *   EA_EUNSUPPORTED, EA_EDEVICE, EA_EHIP   as ea_attn_fwd.
+ * All calls on one GPU share that GPU's array, and it keeps the last call's
+ * contents (every element a launch reads, it first writes, so nothing needs
+ * clearing): launches that may overlap on one GPU (different streams, or
+ * threads without ordering) race on it and must not be issued that way.
+ */
+int ea_attn_fwd_noalloc(const ea_attn_args* args, void* stream);
 
 /*
  * ea_attn_plan -- fill *info with the tile configuration and grid that

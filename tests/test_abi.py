@@ -46,7 +46,7 @@ def test_library_embeds_gpu_code():
 
 def test_abi_version_and_status_strings():
     assert _lib.lib().ea_abi_version() == _lib.EA_ABI_VERSION
-    for code in range(5):
+    for code in range(6):
         assert _lib.status_string(code)
     assert _lib.status_string(99) == "unknown status"
     assert _lib.lib().ea_last_hip_error() == 0
@@ -167,8 +167,9 @@ def test_validation_errors(field, value, code):
     setattr(a, field, value)
     st, _ = plan_status(a)
     assert st == code, (field, value, _lib.status_string(st))
-    # the launch entry point applies the same checks before touching a device
+    # the launch entry points apply the same checks before touching a device
     assert _lib.lib().ea_attn_fwd(ctypes.byref(a), None) == code
+    assert _lib.lib().ea_attn_fwd_noalloc(ctypes.byref(a), None) == code
 
 
 def test_shared_kv_heads():
@@ -377,3 +378,26 @@ def test_python_window_values_are_range_checked():
     for bad in ((-2, 0), (0, -(2 ** 32) + 5), (-(2 ** 40), -1)):
         with pytest.raises(ValueError):
             make_args(x, x, x, x, None, window_size=bad)
+
+
+def test_noalloc_scratch_limit_and_workspace_rules():
+    # the allocation-free forward keeps the key split's partial results in a
+    # 32 MiB static array: a plan that wants more is refused before any
+    # device call, with its own status
+    a = make(B=1, N=32768, H=1, D=128, causal=1)
+    st, info = plan_status(a)
+    assert st == 0 and info.splits == 2
+    assert info.workspace_bytes == 2 * 32768 * 129 * 4 > 32 << 20
+    assert _lib.lib().ea_attn_fwd_noalloc(ctypes.byref(a), None) == _lib.EA_ESCRATCH
+    assert "scratch" in _lib.status_string(_lib.EA_ESCRATCH)
+    with pytest.raises(ValueError):
+        _lib.check(_lib.EA_ESCRATCH)
+    # it takes no caller workspace
+    a = make(workspace=FAKE + 5 * SIZE, workspace_bytes=4096, q_stride_s=-1)   # invalid stride checked first
+    assert _lib.lib().ea_attn_fwd_noalloc(ctypes.byref(a), None) == _lib.EA_EUNSUPPORTED
+    a = make(workspace=FAKE + 5 * SIZE, workspace_bytes=4096)
+    assert _lib.lib().ea_attn_fwd_noalloc(ctypes.byref(a), None) == _lib.EA_EINVAL
+    # an empty problem is fine without pointers
+    e = make(B=0)
+    e.q = e.k = e.v = e.o = 0
+    assert _lib.lib().ea_attn_fwd_noalloc(ctypes.byref(e), None) == _lib.EA_OK
