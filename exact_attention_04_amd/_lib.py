@@ -104,6 +104,26 @@ _lib = None
 _lock = threading.Lock()
 
 
+def bind(h: ctypes.CDLL) -> ctypes.CDLL:
+    """Declare the argument and result types of the exported functions on a
+    loaded library handle."""
+    h.ea_attn_fwd.argtypes = [ctypes.POINTER(AttnArgs), ctypes.c_void_p]
+    h.ea_attn_fwd.restype = ctypes.c_int
+    h.ea_attn_fwd_noalloc.argtypes = [ctypes.POINTER(AttnArgs), ctypes.c_void_p]
+    h.ea_attn_fwd_noalloc.restype = ctypes.c_int
+    h.ea_attn_bwd.argtypes = [ctypes.POINTER(BwdArgs), ctypes.c_void_p]
+    h.ea_attn_bwd.restype = ctypes.c_int
+    h.ea_attn_plan.argtypes = [ctypes.POINTER(AttnArgs), ctypes.POINTER(PlanInfo)]
+    h.ea_attn_plan.restype = ctypes.c_int
+    h.ea_status_string.argtypes = [ctypes.c_int]
+    h.ea_status_string.restype = ctypes.c_char_p
+    h.ea_last_hip_error.argtypes = []
+    h.ea_last_hip_error.restype = ctypes.c_int
+    h.ea_abi_version.argtypes = []
+    h.ea_abi_version.restype = ctypes.c_uint32
+    return h
+
+
 def lib() -> ctypes.CDLL:
     """The loaded library (raises if it has not been built)."""
     global _lib
@@ -115,21 +135,7 @@ def lib() -> ctypes.CDLL:
                 raise RuntimeError(
                     f"{LIB_PATH} is missing: build it with `python -m exact_attention_04_amd.build` "
                     "(there is no non-HIP fallback)")
-            h = ctypes.CDLL(LIB_PATH)
-            h.ea_attn_fwd.argtypes = [ctypes.POINTER(AttnArgs), ctypes.c_void_p]
-            h.ea_attn_fwd.restype = ctypes.c_int
-            h.ea_attn_fwd_noalloc.argtypes = [ctypes.POINTER(AttnArgs), ctypes.c_void_p]
-            h.ea_attn_fwd_noalloc.restype = ctypes.c_int
-            h.ea_attn_bwd.argtypes = [ctypes.POINTER(BwdArgs), ctypes.c_void_p]
-            h.ea_attn_bwd.restype = ctypes.c_int
-            h.ea_attn_plan.argtypes = [ctypes.POINTER(AttnArgs), ctypes.POINTER(PlanInfo)]
-            h.ea_attn_plan.restype = ctypes.c_int
-            h.ea_status_string.argtypes = [ctypes.c_int]
-            h.ea_status_string.restype = ctypes.c_char_p
-            h.ea_last_hip_error.argtypes = []
-            h.ea_last_hip_error.restype = ctypes.c_int
-            h.ea_abi_version.argtypes = []
-            h.ea_abi_version.restype = ctypes.c_uint32
+            h = bind(ctypes.CDLL(LIB_PATH))
             if h.ea_abi_version() != EA_ABI_VERSION:
                 raise RuntimeError(f"{LIB_PATH}: ABI version {h.ea_abi_version()} != {EA_ABI_VERSION}")
             _lib = h

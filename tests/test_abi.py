@@ -17,7 +17,27 @@ from exact_attention_04_amd import _lib
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "ea_attn.h")
 
-pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libea_attn.so not built")
+# The library under test: the in-tree build, or a host-only build of the same
+# C ABI layer (HIP calls and launches stubbed) named by EA_ABI_TEST_LIB, which
+# tests/test_abi_host.py uses to run these tests under AddressSanitizer and
+# UndefinedBehaviorSanitizer.
+HOST_LIB = os.environ.get("EA_ABI_TEST_LIB")
+_handle = None
+
+
+def abi():
+    global _handle
+    if _handle is None:
+        _handle = _lib.bind(ctypes.CDLL(HOST_LIB)) if HOST_LIB else _lib.lib()
+    return _handle
+
+
+def status(code):
+    return abi().ea_status_string(code).decode()
+
+
+pytestmark = pytest.mark.skipif(not HOST_LIB and not os.path.exists(_lib.LIB_PATH), reason="libea_attn.so not built")
+product_only = pytest.mark.skipif(bool(HOST_LIB), reason="checks the in-tree GPU library itself")
 
 FAKE = 0x7F0000000000   # never dereferenced: plan() and failing fwd() calls do not touch memory
 
@@ -31,25 +51,27 @@ def test_header_declares_exactly_the_exports():
     assert header_functions() == sorted(_lib.EXPORTS)
 
 
+@product_only
 def test_library_exports_every_declared_symbol():
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True, check=True).stdout
     syms = {line.split()[-1] for line in out.splitlines() if line.strip()}
     for name in header_functions():
         assert name in syms, f"{name} not exported"
-        assert hasattr(_lib.lib(), name)
+        assert hasattr(abi(), name)
 
 
+@product_only
 def test_library_embeds_gpu_code():
     from exact_attention_04_amd.build import elf_section_names
     assert ".hip_fatbin" in elf_section_names(_lib.LIB_PATH)
 
 
 def test_abi_version_and_status_strings():
-    assert _lib.lib().ea_abi_version() == _lib.EA_ABI_VERSION
+    assert abi().ea_abi_version() == _lib.EA_ABI_VERSION
     for code in range(6):
-        assert _lib.status_string(code)
-    assert _lib.status_string(99) == "unknown status"
-    assert _lib.lib().ea_last_hip_error() == 0
+        assert status(code)
+    assert status(99) == "unknown status"
+    assert abi().ea_last_hip_error() == 0
 
 
 def test_struct_sizes_match_c():
@@ -91,14 +113,14 @@ SIZE = 2 * 300 * 3 * 128 * 4 + 4096   # make()'s spacing of the fake tensors
 def plan_status(a):
     info = _lib.PlanInfo()
     info.struct_size = ctypes.sizeof(_lib.PlanInfo)
-    return _lib.lib().ea_attn_plan(ctypes.byref(a), ctypes.byref(info)), info
+    return abi().ea_attn_plan(ctypes.byref(a), ctypes.byref(info)), info
 
 
 def test_plan_valid_configs():
     for dtype, D in ((_lib.EA_F16, 64), (_lib.EA_BF16, 128), (_lib.EA_FP8_E4M3, 128)):
         for layout in ("bshd", "bhsd"):
             st, info = plan_status(make(dtype=dtype, D=D, layout=layout))
-            assert st == _lib.EA_OK, _lib.status_string(st)
+            assert st == _lib.EA_OK, status(st)
             # four waves of 32 query rows per workgroup
             assert info.block_m == 128 and info.block_n == 64 and info.waves == 4
             assert info.grid == 2 * 3 * math.ceil(300 / 128)
@@ -166,10 +188,10 @@ def test_validation_errors(field, value, code):
     a = make()
     setattr(a, field, value)
     st, _ = plan_status(a)
-    assert st == code, (field, value, _lib.status_string(st))
+    assert st == code, (field, value, status(st))
     # the launch entry points apply the same checks before touching a device
-    assert _lib.lib().ea_attn_fwd(ctypes.byref(a), None) == code
-    assert _lib.lib().ea_attn_fwd_noalloc(ctypes.byref(a), None) == code
+    assert abi().ea_attn_fwd(ctypes.byref(a), None) == code
+    assert abi().ea_attn_fwd_noalloc(ctypes.byref(a), None) == code
 
 
 def test_shared_kv_heads():
@@ -180,7 +202,7 @@ def test_shared_kv_heads():
             setattr(a, f"{t}_stride_b", 300 * hk * 128)
             setattr(a, f"{t}_stride_s", hk * 128)
         st, info = plan_status(a)
-        assert st == _lib.EA_OK, (hk, _lib.status_string(st))
+        assert st == _lib.EA_OK, (hk, status(st))
         assert info.grid == 2 * 8 * math.ceil(300 / 128)
     assert plan_status(make(H=8, nheads_k=3))[0] == _lib.EA_EUNSUPPORTED
 
@@ -223,7 +245,7 @@ def test_version1_structs_are_accepted():
     info.struct_size = _lib.PlanInfo.workspace_bytes.offset
     info.workspace_bytes = 12345
     info.splits = 7
-    assert _lib.lib().ea_attn_plan(ctypes.byref(make(B=1, N=512, H=8, D=64, dtype=_lib.EA_F16)), ctypes.byref(info)) == 0
+    assert abi().ea_attn_plan(ctypes.byref(make(B=1, N=512, H=8, D=64, dtype=_lib.EA_F16)), ctypes.byref(info)) == 0
     assert info.workspace_bytes == 12345 and info.splits == 7 and info.block_m == 128
 
 
@@ -248,7 +270,7 @@ def test_pv_dtype_rules():
     # 16-bit inputs take no pv_dtype
     assert plan_status(make(pv_dtype=_lib.EA_FP8_E4M3))[0] == _lib.EA_EUNSUPPORTED
     assert plan_status(make(pv_dtype=_lib.EA_BF16))[0] == _lib.EA_EUNSUPPORTED
-    assert _lib.lib().ea_attn_fwd(ctypes.byref(make(pv_dtype=_lib.EA_FP8_E4M3)), None) == _lib.EA_EUNSUPPORTED
+    assert abi().ea_attn_fwd(ctypes.byref(make(pv_dtype=_lib.EA_FP8_E4M3)), None) == _lib.EA_EUNSUPPORTED
 
 
 def test_fp8_argument_rules():
@@ -264,17 +286,18 @@ def test_empty_problem_is_ok_without_pointers():
     a.q = a.k = a.v = a.o = 0
     st, info = plan_status(a)
     assert st == _lib.EA_OK and info.grid == 0
-    assert _lib.lib().ea_attn_fwd(ctypes.byref(a), None) == _lib.EA_OK
+    assert abi().ea_attn_fwd(ctypes.byref(a), None) == _lib.EA_OK
     a = make(N=0)
-    assert _lib.lib().ea_attn_fwd(ctypes.byref(a), None) == _lib.EA_OK
+    assert abi().ea_attn_fwd(ctypes.byref(a), None) == _lib.EA_OK
 
 
 def test_plan_rejects_small_info_struct():
     info = _lib.PlanInfo()
     info.struct_size = 4
-    assert _lib.lib().ea_attn_plan(ctypes.byref(make()), ctypes.byref(info)) == _lib.EA_EINVAL
+    assert abi().ea_attn_plan(ctypes.byref(make()), ctypes.byref(info)) == _lib.EA_EINVAL
 
 
+@product_only
 def test_python_wrapper_rejects_cpu_tensors():
     import torch
     from exact_attention_04_amd import attention
@@ -337,7 +360,7 @@ def test_bwd_validation_errors(field, value, code):
     # every failing check returns before a device is queried
     a = make_bwd()
     setattr(a, field, value)
-    assert _lib.lib().ea_attn_bwd(ctypes.byref(a), None) == code, (field, value)
+    assert abi().ea_attn_bwd(ctypes.byref(a), None) == code, (field, value)
 
 
 def test_bwd_empty_problem_is_ok_without_pointers():
@@ -345,7 +368,7 @@ def test_bwd_empty_problem_is_ok_without_pointers():
         a = make_bwd(**fields)
         for t in ("q", "k", "v", "o", "dout", "lse", "delta", "dq", "dk", "dv"):
             setattr(a, t, 0)
-        assert _lib.lib().ea_attn_bwd(ctypes.byref(a), None) == _lib.EA_OK
+        assert abi().ea_attn_bwd(ctypes.byref(a), None) == _lib.EA_OK
 
 
 @pytest.mark.parametrize("causal", [0, 1])
@@ -368,6 +391,7 @@ def test_window_bounds_past_the_sequence_plan_as_unbounded(causal):
     assert st == 0 and info.kv_tiles < plan_status(make(B=1, N=4096, H=2))[1].kv_tiles
 
 
+@product_only
 def test_python_window_values_are_range_checked():
     import torch
     from exact_attention_04_amd.attention import make_args
@@ -388,16 +412,16 @@ def test_noalloc_scratch_limit_and_workspace_rules():
     st, info = plan_status(a)
     assert st == 0 and info.splits == 2
     assert info.workspace_bytes == 2 * 32768 * 129 * 4 > 32 << 20
-    assert _lib.lib().ea_attn_fwd_noalloc(ctypes.byref(a), None) == _lib.EA_ESCRATCH
-    assert "scratch" in _lib.status_string(_lib.EA_ESCRATCH)
+    assert abi().ea_attn_fwd_noalloc(ctypes.byref(a), None) == _lib.EA_ESCRATCH
+    assert "scratch" in status(_lib.EA_ESCRATCH)
     with pytest.raises(ValueError):
         _lib.check(_lib.EA_ESCRATCH)
     # it takes no caller workspace
     a = make(workspace=FAKE + 5 * SIZE, workspace_bytes=4096, q_stride_s=-1)   # invalid stride checked first
-    assert _lib.lib().ea_attn_fwd_noalloc(ctypes.byref(a), None) == _lib.EA_EUNSUPPORTED
+    assert abi().ea_attn_fwd_noalloc(ctypes.byref(a), None) == _lib.EA_EUNSUPPORTED
     a = make(workspace=FAKE + 5 * SIZE, workspace_bytes=4096)
-    assert _lib.lib().ea_attn_fwd_noalloc(ctypes.byref(a), None) == _lib.EA_EINVAL
+    assert abi().ea_attn_fwd_noalloc(ctypes.byref(a), None) == _lib.EA_EINVAL
     # an empty problem is fine without pointers
     e = make(B=0)
     e.q = e.k = e.v = e.o = 0
-    assert _lib.lib().ea_attn_fwd_noalloc(ctypes.byref(e), None) == _lib.EA_OK
+    assert abi().ea_attn_fwd_noalloc(ctypes.byref(e), None) == _lib.EA_OK
