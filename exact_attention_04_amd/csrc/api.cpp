@@ -208,9 +208,17 @@ int validate(const ea_attn_args* a, bool* empty) {
   return EA_OK;
 }
 
-// Kernel configuration (see fwd_kernel.h): 1 for e4m3 P.V, else 0.
+// Kernel configuration (see fwd_kernel.h).  fp8: 1 for the e4m3 P.V, else
+// 0.  16-bit, by the launch's items (query tiles of 128 rows x heads): 0 when
+// they give every CU two workgroups; below that key streams, four streams of
+// 32 rows at d = 64 with fewer than 128 items, else two streams of 128 rows
+// (8 waves, one workgroup per CU: two waves per SIMD).
 int choose_cfg(const ea_attn_args* a) {
-  return (a->in_dtype == EA_FP8_E4M3 && pv_dtype_of(a) == EA_FP8_E4M3) ? 1 : 0;
+  if (a->in_dtype == EA_FP8_E4M3) return pv_dtype_of(a) == EA_FP8_E4M3 ? 1 : 0;
+  const int64_t items = a->batch * a->nheads_q * ((a->seqlen_q + 127) / 128);
+  if (items >= 512) return 0;
+  if (items < 128 && a->headdim == 64) return 3;
+  return 2;
 }
 
 ea::FwdParams make_params(const ea_attn_args* a, int cfg) {
@@ -396,6 +404,10 @@ void count_tiles(const ea::FwdParams& p, int cfg, int64_t* tiles, int64_t* maske
 // Key chunks per query tile this call would use with a large enough workspace,
 // and the workspace that takes.
 int wanted_splits(const ea::FwdParams& p, int cfg, int d, int64_t* bytes) {
+  if (ea::key_streams(cfg) > 1) {   // the streams split the keys within the workgroup
+    *bytes = 0;
+    return 1;
+  }
   int64_t total = 0, masked = 0;
   count_tiles(p, cfg, &total, &masked);
   const int s = ea::choose_splits((int64_t)p.q_tiles * p.batch * p.heads, max_kv_tiles(p, cfg), total);

@@ -45,11 +45,18 @@ int64_t split_workspace_bytes(int splits, int64_t batch_heads, int64_t n, int d)
 constexpr int64_t kScratchBytes = (int64_t)32 << 20;
 hipError_t scratch_address(int dev, void** ptr);
 
-// Kernel configurations, both 128 query rows per workgroup (4 waves of 32
-// rows, two waves per SIMD) and 64 keys per K/V tile: 0, P.V in 16 bits
-// (fp8 V widened exactly to bf16); 1 (fp8 inputs only), P and V in e4m3 on
-// the 8-bit matrix instruction.
+// Kernel configurations (64 keys per K/V tile, 32 query rows per wave):
+//   0: 128 rows per workgroup (4 waves), P.V in 16 bits (fp8 V widened
+//      exactly to bf16); two workgroups per CU, two waves per SIMD;
+//   1: as 0 for fp8 inputs with P and V in e4m3 on the 8-bit instruction;
+//   2, 3 (16-bit inputs): the workgroup's waves form key streams that split
+//      the key tiles and merge in LDS, for launches with few query tiles:
+//      2 streams of 4 row waves (128 rows), or 4 streams of 1 (32 rows,
+//      d = 64 only).
+// tile_bm: query rows per workgroup; key_streams: streams; tile_waves: all
+// waves of the workgroup.
 int tile_bm(int cfg);
+int key_streams(int cfg);
 int tile_waves(int cfg);
 int tile_bn();
 int lds_bytes(int in_dtype, int d, int cfg);

@@ -52,11 +52,12 @@
 
 namespace ea {
 
-template <In IN, int D, int WAVES, int RB, bool P8>
+template <In IN, int D, int WAVES, int RB, bool P8, int KS>
 struct Cfg {
   static constexpr bool kFp8 = (IN == In::FP8);
   static_assert(!P8 || (kFp8 && D == 128), "e4m3 P.V: fp8 inputs, d = 128");
-  static constexpr int kThreads = 64 * WAVES;
+  static_assert(KS == 1 || !kFp8, "key streams: 16-bit inputs");
+  static constexpr int kThreads = 64 * WAVES;                 // one key stream's threads
   static constexpr int kBM = 32 * RB * WAVES;        // query rows per workgroup
   static constexpr int kInBytes = kFp8 ? 1 : 2;
   static constexpr int kKRow = D * kInBytes;         // bytes per K row in LDS
@@ -81,10 +82,10 @@ struct Cfg {
 // conflicts.
 __device__ __forceinline__ int v8_swz(int row) { return (row & 3) | (((row >> 3) & 1) << 2); }
 
-template <In IN, int D, int WAVES, int RB, bool P8>
-__global__ void __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(3 - RB, 3 - RB)))
+template <In IN, int D, int WAVES, int RB, bool P8, int KS>
+__global__ void __launch_bounds__(64 * WAVES * KS) __attribute__((amdgpu_waves_per_eu(3 - RB, 3 - RB)))
 attn_fwd_kernel(const FwdParams p) {
-  using C = Cfg<IN, D, WAVES, RB, P8>;
+  using C = Cfg<IN, D, WAVES, RB, P8, KS>;
   constexpr In PIN = (IN == In::F16) ? In::F16 : In::BF16;   // type of P, V in LDS and O
   constexpr int kBM = C::kBM;
   // LDS: two K slots and two V slots.  K of tile i+1 and V of tile i are
@@ -95,13 +96,29 @@ attn_fwd_kernel(const FwdParams p) {
   // tell the DMA into one slot from the reads of another: in a single array
   // it cannot, and it then waits for the DMA just issued before the first
   // read, which serialises the prefetch with the compute.
-  __shared__ __attribute__((aligned(1024))) unsigned char kbuf0[C::kKTile];
-  __shared__ __attribute__((aligned(1024))) unsigned char kbuf1[C::kKTile];
-  __shared__ __attribute__((aligned(1024))) unsigned char vbuf0[C::kVTile];
-  __shared__ __attribute__((aligned(1024))) unsigned char vbuf1[C::kVTile];
+  //
+  // Key streams (KS > 1): the workgroup's waves form KS groups of WAVES waves,
+  // each covering all of the workgroup's query rows over every KS-th key tile
+  // with slots of its own; at the end the streams' partial results (row
+  // maximum, row sum, O) are merged through LDS.  This fills the GPU when the
+  // query tiles alone are too few (short sequences, few heads).
+  __shared__ __attribute__((aligned(1024))) unsigned char kbuf0_s[KS][C::kKTile];
+  __shared__ __attribute__((aligned(1024))) unsigned char kbuf1_s[KS][C::kKTile];
+  __shared__ __attribute__((aligned(1024))) unsigned char vbuf0_s[KS][C::kVTile];
+  __shared__ __attribute__((aligned(1024))) unsigned char vbuf1_s[KS][C::kVTile];
 
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, kept in an SGPR
+  const int tid_all = threadIdx.x;
+  const int wave_all = __builtin_amdgcn_readfirstlane(tid_all >> 6);   // wave-uniform, kept in an SGPR
+  const int stream = KS == 1 ? 0 : wave_all / WAVES;                   // this wave's key stream
+  const int wave = wave_all - stream * WAVES;                           // its row block within the stream
+  const int tid = tid_all - stream * C::kThreads;                       // thread index within the stream
+  unsigned char* const kbuf0 = kbuf0_s[stream];
+  unsigned char* const kbuf1 = kbuf1_s[stream];
+  unsigned char* const vbuf0 = vbuf0_s[stream];
+  unsigned char* const vbuf1 = vbuf1_s[stream];
+  static_assert(KS == 1 || RB == 1, "key streams: one row block per wave (O fits a slot)");
+  // per stream, row block and row: the row's maximum and sum, for the merge
+  __shared__ float merge_ml[KS][WAVES][RB][2][32];
   const int lane = tid & 63;
   const int half = lane >> 5;      // which 16 of each 32 keys this lane holds
   const int col = lane & 31;       // the query row (within each row block) this lane owns
@@ -143,6 +160,12 @@ attn_fwd_kernel(const FwdParams p) {
   const int kt_count = (kr.hi + kBN - 1) / kBN - kt_first;
   const int kt_begin = kt_first + (int)((int64_t)kt_count * chunk / p.splits);
   const int kt_end = kt_first + (int)((int64_t)kt_count * (chunk + 1) / p.splits);
+  // This stream's key tiles: kt_begin + stream + KS i for i < iters.  Every
+  // stream runs `iters` iterations, so that each wave meets each barrier; only
+  // a stream's last tile can lie past kt_end, and that one is loaded as zeros
+  // and not computed.
+  const int iters = (kt_end - kt_begin + KS - 1) / KS;
+  const int kt_first_s = kt_begin + stream;
 
   // ---- this wave's rows: RB blocks of 32, lane `col` owns one row in each
   const int wr0 = q0 + wave * 32 * RB;     // first row of the wave
@@ -704,11 +727,13 @@ attn_fwd_kernel(const FwdParams p) {
   auto iter = [&](int kt, const unsigned char* kread, const unsigned char* vread, unsigned char* kwrite,
                   unsigned char* vwrite) __attribute__((always_inline)) {
     if (wave_needs_ref()) fold_max(s_a, s_b);
-    const bool m_next = tile_masked(kt + 1);
+    const int kt_next = kt + KS;     // this stream's next tile
+    const bool m_next = tile_masked(kt_next);
     f32x16 n_a[RB], n_b[RB];
-    // K(kt+2) (zeros past the last tile) and V(kt+1), into the slots the
-    // previous iteration freed, spread over the S MFMAs of the first unit
-    const TileRange rk = k_range(kt + 2), rv = v_range(kt + 1);
+    // K of the tile after next (zeros past the last tile) and V of the next,
+    // into the slots the previous iteration freed, spread over the S MFMAs of
+    // the first unit
+    const TileRange rk = k_range(kt_next + KS), rv = v_range(kt_next);
     constexpr int kPer = (kDmaK + kDmaV + C::kQSteps - 1) / C::kQSteps;
     auto dma_hook = [&](int st) {
 #pragma unroll
@@ -724,15 +749,15 @@ attn_fwd_kernel(const FwdParams p) {
       for (int qb = 0; qb < RB; ++qb) l_tile[qb] = l_part[qb];
       uint32_t pa[RB][4], pb[RB][4];
       unit8(BoolTag<true>{}, s_a, 0, kread, n_a, pa, dma_hook);
-      if (m_next) apply_mask(n_a, (kt + 1) * kBN, 0);
+      if (m_next) apply_mask(n_a, kt_next * kBN, 0);
       unit8(BoolTag<true>{}, s_b, 1, kread, n_b, pb, [](int) {});
-      if (m_next) apply_mask(n_b, (kt + 1) * kBN, 1);
+      if (m_next) apply_mask(n_b, kt_next * kBN, 1);
       tile_pv8(s_a, s_b, pa, pb, l_tile, vread);
     } else {
       unit(BoolTag<true>{}, s_a, 0, vread, kread, n_a, dma_hook);
-      if (m_next) apply_mask(n_a, (kt + 1) * kBN, 0);
+      if (m_next) apply_mask(n_a, kt_next * kBN, 0);
       unit(BoolTag<true>{}, s_b, 1, vread, kread, n_b, [](int) {});
-      if (m_next) apply_mask(n_b, (kt + 1) * kBN, 1);
+      if (m_next) apply_mask(n_b, kt_next * kBN, 1);
     }
 #pragma unroll
     for (int qb = 0; qb < RB; ++qb) {
@@ -744,46 +769,49 @@ attn_fwd_kernel(const FwdParams p) {
     __syncthreads();
   };
   auto key_loop = [&]() __attribute__((always_inline)) {
-    if (kt_begin >= kt_end) return;
-    issue_k(kt_begin, kbuf0);
-    issue_v(kt_begin, vbuf0);
-    issue_k(kt_begin + 1, kbuf1);   // zeros if there is no second tile
+    if (iters <= 0) return;   // no visible key tile (the same in every stream)
+    issue_k(kt_first_s, kbuf0);
+    issue_v(kt_first_s, vbuf0);
+    issue_k(kt_first_s + KS, kbuf1);   // zeros if there is no second tile
     store_v_fp8(vbuf0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     s_half(kbuf0, 0, s_a, [](int) {});
     s_half(kbuf0, 1, s_b, [](int) {});
-    if (tile_masked(kt_begin)) {
-      apply_mask(s_a, kt_begin * kBN, 0);
-      apply_mask(s_b, kt_begin * kBN, 1);
+    if (tile_masked(kt_first_s)) {
+      apply_mask(s_a, kt_first_s * kBN, 0);
+      apply_mask(s_b, kt_first_s * kBN, 1);
     }
-    __syncthreads();   // every wave is done with K(kt_begin) before its slot is refilled
+    __syncthreads();   // every wave is done with the first K tile before its slot is refilled
     // tiles with a successor: pairs (static slot names), then an odd one
-    const int with_next = kt_end - 1 - kt_begin;
-    int kt = kt_begin;
-    for (int j = 0; j < with_next / 2; ++j, kt += 2) {
+    const int with_next = iters - 1;
+    int kt = kt_first_s;
+    for (int j = 0; j < with_next / 2; ++j, kt += 2 * KS) {
       iter(kt, kbuf1, vbuf0, kbuf0, vbuf1);
-      iter(kt + 1, kbuf0, vbuf1, kbuf1, vbuf0);
+      iter(kt + KS, kbuf0, vbuf1, kbuf1, vbuf0);
     }
     const bool odd = (with_next & 1) != 0;
     if (odd) {
       iter(kt, kbuf1, vbuf0, kbuf0, vbuf1);
-      ++kt;
+      kt += KS;
     }
-    // last tile: softmax and P.V only
+    // last tile: softmax and P.V only (none if this stream's last tile lies
+    // past the range)
     const unsigned char* vlast = odd ? vbuf1 : vbuf0;
-    if (wave_needs_ref()) fold_max(s_a, s_b);
-    if constexpr (P8) {
-      float l_tile[RB];
+    if (kt < kt_end) {
+      if (wave_needs_ref()) fold_max(s_a, s_b);
+      if constexpr (P8) {
+        float l_tile[RB];
 #pragma unroll
-      for (int qb = 0; qb < RB; ++qb) l_tile[qb] = l_part[qb];
-      uint32_t pa[RB][4], pb[RB][4];
-      unit8(BoolTag<false>{}, s_a, 0, kbuf0, s_a, pa, [](int) {});
-      unit8(BoolTag<false>{}, s_b, 1, kbuf0, s_b, pb, [](int) {});
-      tile_pv8(s_a, s_b, pa, pb, l_tile, vlast);
-    } else {
-      unit(BoolTag<false>{}, s_a, 0, vlast, kbuf0, s_a, [](int) {});
-      unit(BoolTag<false>{}, s_b, 1, vlast, kbuf0, s_b, [](int) {});
+        for (int qb = 0; qb < RB; ++qb) l_tile[qb] = l_part[qb];
+        uint32_t pa[RB][4], pb[RB][4];
+        unit8(BoolTag<false>{}, s_a, 0, kbuf0, s_a, pa, [](int) {});
+        unit8(BoolTag<false>{}, s_b, 1, kbuf0, s_b, pb, [](int) {});
+        tile_pv8(s_a, s_b, pa, pb, l_tile, vlast);
+      } else {
+        unit(BoolTag<false>{}, s_a, 0, vlast, kbuf0, s_a, [](int) {});
+        unit(BoolTag<false>{}, s_b, 1, vlast, kbuf0, s_b, [](int) {});
+      }
     }
     __syncthreads();   // the slots are reused by a second pass
   };
@@ -791,18 +819,21 @@ attn_fwd_kernel(const FwdParams p) {
   // tile at a time, no prefetch.
   float m_exact[RB];
   auto max_loop = [&]() {
-    for (int kt = kt_begin; kt < kt_end; ++kt) {
+    for (int i = 0; i < iters; ++i) {
+      const int kt = kt_first_s + KS * i;
       issue_k(kt, kbuf0);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      const bool masked = tile_masked(kt);
+      if (kt < kt_end) {
+        const bool masked = tile_masked(kt);
 #pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        f32x16 s[RB];
-        s_half(kbuf0, hb, s, [](int) {});
-        if (masked) apply_mask(s, kt * kBN, hb);
+        for (int hb = 0; hb < 2; ++hb) {
+          f32x16 s[RB];
+          s_half(kbuf0, hb, s, [](int) {});
+          if (masked) apply_mask(s, kt * kBN, hb);
 #pragma unroll
-        for (int qb = 0; qb < RB; ++qb) m_exact[qb] = fmaxf(m_exact[qb], block_max(s[qb]));
+          for (int qb = 0; qb < RB; ++qb) m_exact[qb] = fmaxf(m_exact[qb], block_max(s[qb]));
+        }
       }
       __syncthreads();
     }
@@ -830,8 +861,22 @@ attn_fwd_kernel(const FwdParams p) {
     for (int qb = 0; qb < RB; ++qb) m_exact[qb] = -INFINITY;
     max_loop();
 #pragma unroll
+    for (int qb = 0; qb < RB; ++qb) m_exact[qb] = pair_max(m_exact[qb]);
+    if constexpr (KS > 1) {
+      // the exact maximum over all key streams
+#pragma unroll
+      for (int qb = 0; qb < RB; ++qb)
+        if (half == 0) merge_ml[stream][wave][qb][0][col] = m_exact[qb];
+      __syncthreads();
+#pragma unroll
+      for (int qb = 0; qb < RB; ++qb)
+#pragma unroll
+        for (int ss = 0; ss < KS; ++ss) m_exact[qb] = fmaxf(m_exact[qb], merge_ml[ss][wave][qb][0][col]);
+      __syncthreads();
+    }
+#pragma unroll
     for (int qb = 0; qb < RB; ++qb) {
-      const float m = pair_max(m_exact[qb]);
+      const float m = m_exact[qb];
       m_run[qb] = m;
       neg_mc[qb] = (m == -INFINITY) ? 0.f : -m * cexp + kPShift;
       l_part[qb] = 0.f;
@@ -842,10 +887,57 @@ attn_fwd_kernel(const FwdParams p) {
     }
   }
 
+  float l_fin[RB];
+#pragma unroll
+  for (int qb = 0; qb < RB; ++qb) l_fin[qb] = pair_sum(l_part[qb]);
+  if constexpr (KS > 1) {
+    // Merge of the key streams: each stream's O, l are relative to its own
+    // reference m_s; with M the largest, O = sum_s 2^((m_s - M) c) O_s and
+    // l likewise.  Streams 1.. pass theirs to stream 0 through LDS (each wave
+    // through its own stream's slot; the slots are free after the key loop's
+    // final barrier), and stream 0 writes the result.
+    unsigned char* const own = wave == 0 ? kbuf0 : wave == 1 ? kbuf1 : wave == 2 ? vbuf0 : vbuf1;
+    if (stream > 0) {
+      float* dst = (float*)own;
+#pragma unroll
+      for (int c = 0; c < C::kDBlocks; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dst[(16 * c + r) * 64 + lane] = acc[0][c][r];
+      if (half == 0) {
+        merge_ml[stream][wave][0][0][col] = m_run[0];
+        merge_ml[stream][wave][0][1][col] = l_fin[0];
+      }
+    }
+    __syncthreads();
+    if (stream > 0) return;   // no barrier follows
+    float m_all = m_run[0];
+#pragma unroll
+    for (int ss = 1; ss < KS; ++ss) m_all = fmaxf(m_all, merge_ml[ss][wave][0][0][col]);
+    auto weight = [&](float m_s) { return m_s == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_s - m_all) * cexp); };
+    const float f0 = weight(m_run[0]);
+    l_fin[0] *= f0;
+#pragma unroll
+    for (int c = 0; c < C::kDBlocks; ++c)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[0][c][r] *= f0;
+#pragma unroll
+    for (int ss = 1; ss < KS; ++ss) {
+      const float fs = weight(merge_ml[ss][wave][0][0][col]);
+      l_fin[0] = __builtin_fmaf(fs, merge_ml[ss][wave][0][1][col], l_fin[0]);
+      const unsigned char* theirs = wave == 0 ? kbuf0_s[ss] : wave == 1 ? kbuf1_s[ss] : wave == 2 ? vbuf0_s[ss] : vbuf1_s[ss];
+      const float* src = (const float*)theirs;
+#pragma unroll
+      for (int c = 0; c < C::kDBlocks; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[0][c][r] = __builtin_fmaf(fs, src[(16 * c + r) * 64 + lane], acc[0][c][r]);
+    }
+    m_run[0] = m_all;
+  }
+
   // ---- epilogue: O = O_acc / l (* v descale), LSE = ln(2) * (m c + log2 l)
 #pragma unroll
   for (int qb = 0; qb < RB; ++qb) {
-    const float l_row = pair_sum(l_part[qb]);
+    const float l_row = l_fin[qb];
     if (qrow[qb] < n && p.splits > 1) {
       // partial result of this key chunk: normalised O in fp32 and its LSE,
       // merged by attn_fwd_combine
@@ -957,11 +1049,11 @@ hipError_t scratch_address(int dev, void** ptr) {
   return status[dev];
 }
 
-template <In IN, int D, int WAVES, int RB, bool P8 = false>
+template <In IN, int D, int WAVES, int RB, bool P8, int KS>
 static hipError_t launch_t(const FwdParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)((int64_t)p.q_tiles * p.batch * p.heads * p.splits));
-  const dim3 block(64 * WAVES);
-  hipLaunchKernelGGL((attn_fwd_kernel<IN, D, WAVES, RB, P8>), grid, block, 0, stream, p);
+  const dim3 block(64 * WAVES * KS);
+  hipLaunchKernelGGL((attn_fwd_kernel<IN, D, WAVES, RB, P8, KS>), grid, block, 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
   constexpr In OUT = (IN == In::F16) ? In::F16 : In::BF16;
@@ -972,18 +1064,30 @@ static hipError_t launch_t(const FwdParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// The 16-bit configurations by key streams: row waves per stream, streams.
+template <In IN, int D>
+static hipError_t launch_16bit(const FwdParams& p, int cfg, hipStream_t stream) {
+  switch (cfg) {
+    case 0: return launch_t<IN, D, 4, 1, false, 1>(p, stream);
+    case 2: return launch_t<IN, D, 4, 1, false, 2>(p, stream);
+    // four streams only at d = 64: four times two K and two V slots must fit a CU's LDS
+    case 3: if constexpr (D == 64) return launch_t<IN, D, 1, 1, false, 4>(p, stream); else return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
+}
+
 hipError_t launch_fwd(const FwdParams& p, int in_dtype, int d, int cfg, hipStream_t stream) {
   // in_dtype: 1 = f16, 2 = bf16, 3 = fp8 e4m3 (validated by the caller)
-  if (cfg == 1) {
-    if (in_dtype == 3 && d == 128) return launch_t<In::FP8, 128, 4, 1, true>(p, stream);
+  if (in_dtype == 3) {
+    if (d != 128) return hipErrorInvalidValue;
+    if (cfg == 0) return launch_t<In::FP8, 128, 4, 1, false, 1>(p, stream);
+    if (cfg == 1) return launch_t<In::FP8, 128, 4, 1, true, 1>(p, stream);
     return hipErrorInvalidValue;
   }
-  if (cfg != 0) return hipErrorInvalidValue;
-  if (in_dtype == 1 && d == 64) return launch_t<In::F16, 64, 4, 1>(p, stream);
-  if (in_dtype == 1 && d == 128) return launch_t<In::F16, 128, 4, 1>(p, stream);
-  if (in_dtype == 2 && d == 64) return launch_t<In::BF16, 64, 4, 1>(p, stream);
-  if (in_dtype == 2 && d == 128) return launch_t<In::BF16, 128, 4, 1>(p, stream);
-  if (in_dtype == 3 && d == 128) return launch_t<In::FP8, 128, 4, 1>(p, stream);
+  if (in_dtype == 1 && d == 64) return launch_16bit<In::F16, 64>(p, cfg, stream);
+  if (in_dtype == 1 && d == 128) return launch_16bit<In::F16, 128>(p, cfg, stream);
+  if (in_dtype == 2 && d == 64) return launch_16bit<In::BF16, 64>(p, cfg, stream);
+  if (in_dtype == 2 && d == 128) return launch_16bit<In::BF16, 128>(p, cfg, stream);
   return hipErrorInvalidValue;
 }
 

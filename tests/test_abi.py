@@ -117,15 +117,45 @@ def plan_status(a):
 
 
 def test_plan_valid_configs():
-    for dtype, D in ((_lib.EA_F16, 64), (_lib.EA_BF16, 128), (_lib.EA_FP8_E4M3, 128)):
+    # B2 H3 N300 has few query tiles (18 items of 128 rows): 16-bit inputs run
+    # key streams (4 x 32 rows at d = 64, 2 x 128 rows at d = 128), fp8 the
+    # plain 128-row configuration
+    for dtype, D, bm, waves, name in ((_lib.EA_F16, 64, 32, 4, "attn_fwd<f16,d64,bm32,bn64,ks4>"),
+                                      (_lib.EA_BF16, 128, 128, 8, "attn_fwd<bf16,d128,bm128,bn64,ks2>"),
+                                      (_lib.EA_FP8_E4M3, 128, 128, 4, "attn_fwd<fp8,d128,bm128,bn64>")):
         for layout in ("bshd", "bhsd"):
             st, info = plan_status(make(dtype=dtype, D=D, layout=layout))
             assert st == _lib.EA_OK, status(st)
-            # four waves of 32 query rows per workgroup
-            assert info.block_m == 128 and info.block_n == 64 and info.waves == 4
-            assert info.grid == 2 * 3 * math.ceil(300 / 128)
-            assert info.kernel.decode().startswith("attn_fwd<")
+            assert (info.block_m, info.block_n, info.waves) == (bm, 64, waves)
+            assert info.grid == 2 * 3 * math.ceil(300 / bm)
+            assert info.kernel.decode() == name
             assert info.lds_bytes <= 160 * 1024
+
+
+def test_plan_configuration_by_launch_size():
+    # 16-bit: two workgroups of 128 rows per CU (512 items) keep the plain
+    # configuration; fewer items take key streams
+    for (B, N, H, D), name in (((4, 4096, 32, 128), "attn_fwd<bf16,d128,bm128,bn64>"),
+                               ((2, 1024, 32, 128), "attn_fwd<bf16,d128,bm128,bn64>"),
+                               ((2, 1024, 16, 128), "attn_fwd<bf16,d128,bm128,bn64,ks2>"),
+                               ((1, 512, 8, 128), "attn_fwd<bf16,d128,bm128,bn64,ks2>"),
+                               ((2, 2048, 8, 64), "attn_fwd<bf16,d64,bm128,bn64,ks2>"),
+                               ((1, 1920, 8, 64), "attn_fwd<bf16,d64,bm32,bn64,ks4>"),
+                               ((1, 512, 8, 64), "attn_fwd<bf16,d64,bm32,bn64,ks4>")):
+        a = make(B=B, N=N, H=H, D=D, causal=1)
+        for t in "qkvo":
+            setattr(a, f"{t}_stride_b", N * H * D)
+            setattr(a, f"{t}_stride_s", H * D)
+            setattr(a, f"{t}_stride_h", D)
+        for t, i in zip("qkvo", range(4)):
+            setattr(a, t, FAKE + i * (B * N * H * D * 2 + 4096))
+        a.lse = FAKE + 4 * (B * N * H * D * 2 + 4096)
+        a.lse_stride_b, a.lse_stride_h = H * N, N
+        st, info = plan_status(a)
+        assert st == 0, ((B, N, H, D), status(st))
+        assert info.kernel.decode() == name, ((B, N, H, D), info.kernel)
+        waves = 8 if "ks2" in name else 4
+        assert info.waves == waves and info.splits == 1 and info.workspace_bytes == 0
 
 
 def test_plan_headline_shape():
@@ -208,16 +238,21 @@ def test_shared_kv_heads():
 
 
 def test_key_split_plan_and_workspace_rules():
-    # balanced work (no mask) is not split, however few the query tiles
-    st, info = plan_status(make(B=1, N=512, H=8, D=64, dtype=_lib.EA_F16))
-    assert st == 0 and info.splits == 1 and info.workspace_bytes == 0
-    # causal B2 H8 N2048: 256 items, the heaviest tile sees 32 key tiles
-    # against 17 on average -> 2 chunks
+    fp8 = _lib.EA_FP8_E4M3
+    # 16-bit launches with few query tiles split their keys inside the
+    # workgroup (key streams): no workspace
     st, info = plan_status(make(B=2, N=2048, H=8, D=64, dtype=_lib.EA_F16, causal=1))
+    assert st == 0 and info.splits == 1 and info.workspace_bytes == 0 and "ks2" in info.kernel.decode()
+    # fp8: balanced work (no mask) is not split, however few the query tiles
+    st, info = plan_status(make(B=1, N=512, H=8, D=128, dtype=fp8))
+    assert st == 0 and info.splits == 1 and info.workspace_bytes == 0
+    # causal fp8 B1 H8 N2048: 128 items, the heaviest tile sees 32 key tiles
+    # against 17 on average -> 2 chunks
+    st, info = plan_status(make(B=1, N=2048, H=8, D=128, dtype=fp8, causal=1))
     assert st == 0 and info.splits == 2
-    assert info.workspace_bytes == 2 * 16 * 2048 * (64 + 1) * 4
-    # causal B1 H2 N1000: 16 items -> up to 8 chunks, capped by the balance rule
-    st, info = plan_status(make(B=1, N=1000, H=2, D=128, causal=1))
+    assert info.workspace_bytes == 2 * 8 * 2048 * (128 + 1) * 4
+    # causal fp8 B1 H2 N1000: 16 items -> up to 8 chunks, capped by the balance rule
+    st, info = plan_status(make(B=1, N=1000, H=2, D=128, causal=1, dtype=fp8))
     assert st == 0 and info.splits == 2
     # the headline shape fills the GPU: no split, no workspace
     st, info = plan_status(make(B=4, N=4096, H=32, causal=1))
@@ -246,7 +281,7 @@ def test_version1_structs_are_accepted():
     info.workspace_bytes = 12345
     info.splits = 7
     assert abi().ea_attn_plan(ctypes.byref(make(B=1, N=512, H=8, D=64, dtype=_lib.EA_F16)), ctypes.byref(info)) == 0
-    assert info.workspace_bytes == 12345 and info.splits == 7 and info.block_m == 128
+    assert info.workspace_bytes == 12345 and info.splits == 7 and info.block_m == 32
 
 
 def test_version2_structs_are_accepted():
@@ -408,7 +443,7 @@ def test_noalloc_scratch_limit_and_workspace_rules():
     # the allocation-free forward keeps the key split's partial results in a
     # 32 MiB static array: a plan that wants more is refused before any
     # device call, with its own status
-    a = make(B=1, N=32768, H=1, D=128, causal=1)
+    a = make(B=1, N=32768, H=1, D=128, causal=1, dtype=_lib.EA_FP8_E4M3)
     st, info = plan_status(a)
     assert st == 0 and info.splits == 2
     assert info.workspace_bytes == 2 * 32768 * 129 * 4 > 32 << 20

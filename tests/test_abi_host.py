@@ -70,9 +70,9 @@ def _args():
 
 
 def _split_args():
-    # causal B1 H2 N1000: the plan splits the keys (its workspace is 2 chunks)
+    # causal fp8 B1 H2 N1000: the plan splits the keys (its workspace is 2 chunks)
     from test_abi import make
-    return make(B=1, N=1000, H=2, D=128, causal=1)
+    return make(B=1, N=1000, H=2, D=128, causal=1, dtype=_lib.EA_FP8_E4M3)
 
 
 def _bwd_args():

@@ -148,22 +148,63 @@ def test_key_split_masks(n, d, dtype, mask):
 
 @pytest.mark.parametrize("window", [(-1, -1), (1000, -1)])
 @pytest.mark.parametrize("layout", ["bshd", "bhsd"])
-@pytest.mark.parametrize("dtype,d,heads,heads_kv", [("bf16", 128, 8, 2), ("f16", 64, 4, 1)])
+@pytest.mark.parametrize("dtype,d,heads,heads_kv", [("bf16", 128, 8, 2), ("f16", 64, 4, 1), ("fp8", 128, 8, 2)])
 def test_key_split_with_shared_kv_heads(dtype, d, heads, heads_kv, layout, window):
-    # causal launches the planner does split (plain, and with a window of
-    # 1000 keys that still leaves the tiles unbalanced), with query heads
-    # sharing K/V heads
+    # causal launches with few query tiles, plain and with a window of 1000
+    # keys that still leaves the tiles unbalanced, with query heads sharing
+    # K/V heads: 16-bit inputs split the keys among key streams inside the
+    # workgroup, fp8 among workgroups (chunks merged by a second kernel)
     from exact_attention_04_amd import plan
     from parity_helpers import upload
     causal = True
     inp = small_case(1, heads, 1100, d, dtype, layout, 8100 + heads + d, heads_kv=heads_kv)
     q, k, v = upload(inp)
-    o = torch.empty_like(q)
+    o = torch.empty(q.shape, dtype=torch.bfloat16 if dtype == "fp8" else q.dtype, device=q.device)
     (B, N, H) = (1, 1100, heads)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    assert plan(q, k, v, o, lse, causal=causal, window_size=window, layout=layout).splits > 1
+    info = plan(q, k, v, o, lse, causal=causal, window_size=window, layout=layout,
+                descale=inp.descale if dtype == "fp8" else None)
+    kernel, splits = info.kernel.decode(), info.splits
+    if dtype == "fp8":
+        assert splits > 1, kernel
+    else:
+        assert ",ks" in kernel and splits == 1, kernel
     full_check(inp, dtype, causal=causal, window=window, layout=layout, split_kv=True,
                what=f"split {dtype} H{heads}/Hk{heads_kv} {layout} window {window}")
+
+
+@pytest.mark.parametrize("mask", list(MASKS))
+@pytest.mark.parametrize("n", [1, 63, 129, 333])
+@pytest.mark.parametrize("dtype,d", [("f16", 64), ("bf16", 128)])
+def test_plain_configuration_small_shapes(dtype, d, n, mask):
+    # enough (batch, head) pairs that the launch keeps the plain 128-row
+    # configuration (at least 512 query tiles x heads), with ragged tails and
+    # every mask kind; the small sweeps above run with key streams
+    from exact_attention_04_amd import plan
+    from parity_helpers import upload
+    causal, window = MASKS[mask]
+    B, H = (8, 32) if n > 128 else (16, 32)
+    inp = small_case(B, H, n, d, dtype, "bshd", 9300 + n + d + 3 * list(MASKS).index(mask))
+    q, k, v = upload(inp)
+    kernel = plan(q, k, v, torch.empty_like(q), causal=causal, window_size=window).kernel.decode()
+    assert ",ks" not in kernel, kernel
+    full_check(inp, dtype, causal=causal, window=window, what=f"plain {dtype} d{d} n{n} {mask}")
+
+
+@pytest.mark.parametrize("n", [65, 200, 330, 1000])
+@pytest.mark.parametrize("causal,window", [(False, (-1, -1)), (True, (-1, -1)), (True, (130, 0)), (False, (70, 70))])
+@pytest.mark.parametrize("dtype,d", [("f16", 64), ("bf16", 128)])
+def test_key_streams_uneven_tiles(dtype, d, n, causal, window):
+    # key tile counts that do not divide among the streams (a stream's last
+    # tile past the range is loaded as zeros and skipped), query tiles whose
+    # visible keys fit in fewer tiles than there are streams
+    from exact_attention_04_amd import plan
+    from parity_helpers import upload
+    inp = small_case(1, 2, n, d, dtype, "bshd", 9500 + n + d)
+    q, k, v = upload(inp)
+    kernel = plan(q, k, v, torch.empty_like(q), causal=causal, window_size=window).kernel.decode()
+    assert (",ks4" if d == 64 else ",ks2") in kernel, kernel
+    full_check(inp, dtype, causal=causal, window=window, what=f"streams {dtype} d{d} n{n} {causal} {window}")
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])

@@ -124,14 +124,27 @@ def test_no_device_allocation():
     attention(q, k, v, causal=True, out=o, lse=lse, split_kv=False)
     torch.cuda.synchronize()
     assert torch.cuda.max_memory_allocated() == before
-    # with the key split (64 query tiles x heads here) the only extra memory is
-    # the planned scratch: chunks x B x H x N x (D + 1) float32, linear in N
+    # 16-bit launches with few query tiles split their keys among key streams
+    # inside the workgroup: still nothing allocated
     from exact_attention_04_amd import plan
     info = plan(q, k, v, o, lse, causal=True)
-    assert info.splits > 1
+    assert info.splits == 1 and info.workspace_bytes == 0
     torch.cuda.reset_peak_memory_stats()
     before = torch.cuda.memory_allocated()
     attention(q, k, v, causal=True, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.cuda.max_memory_allocated() == before
+    # with the key split among workgroups (fp8, 64 query tiles x heads here)
+    # the only extra memory is the planned scratch: chunks x B x H x N x
+    # (D + 1) float32, linear in N
+    inp8 = small_case(2, 4, 1024, 128, "fp8", "bshd", 5)
+    q8, k8, v8 = _gpu(inp8)
+    o8 = torch.empty(q8.shape, dtype=torch.bfloat16, device="cuda")
+    info = plan(q8, k8, v8, o8, lse, causal=True, descale=inp8.descale)
+    assert info.splits > 1
+    torch.cuda.reset_peak_memory_stats()
+    before = torch.cuda.memory_allocated()
+    attention(q8, k8, v8, causal=True, out=o8, lse=lse, descale=inp8.descale)
     torch.cuda.synchronize()
     extra = torch.cuda.max_memory_allocated() - before
     assert info.workspace_bytes <= extra <= info.workspace_bytes + (2 << 20)

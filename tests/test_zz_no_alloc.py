@@ -2,7 +2,9 @@
 C ABI: its output against ea_attn_fwd's on the same inputs (the same kernels
 and key split, so the same bits), two calls in a row with the second on a
 smaller problem (the static scratch keeps the first call's contents), and the
-float64 oracle's tolerance on the second."""
+float64 oracle's tolerance on the second.  The split launches are fp8 ones:
+16-bit launches with few query tiles split their keys inside the workgroup
+and need no scratch."""
 import numpy as np
 import pytest
 import torch
@@ -23,7 +25,7 @@ def _gpu(inp):
 
 def _noalloc(q, k, v, **kw):
     (B, N, H) = (q.shape[0], q.shape[1], q.shape[2]) if kw.get("layout", "bshd") == "bshd" else (q.shape[0], q.shape[2], q.shape[1])
-    o = torch.empty_like(q)
+    o = torch.empty(q.shape, dtype=torch.bfloat16 if q.dtype == torch.float8_e4m3fn else q.dtype, device=q.device)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     a = make_args(q, k, v, o, lse, **kw)
     st = _lib.fwd_noalloc(a, torch.cuda.current_stream().cuda_stream)
@@ -33,15 +35,19 @@ def _noalloc(q, k, v, **kw):
 
 @pytest.mark.parametrize("order", ["large_then_small", "small_then_large"])
 def test_noalloc_equals_the_workspace_entry_point(order):
+    # fp8 launches with few query tiles split their keys among workgroups
+    # (16-bit ones use key streams inside the workgroup and need no scratch)
     cases = [
-        (small_case(1, 8, 2048, 64, "f16", "bhsd", 31), dict(causal=True, layout="bhsd", softmax_scale=0.125)),
-        (small_case(1, 2, 1000, 128, "bf16", "bshd", 32), dict(causal=True, window_size=(700, -1))),
+        (small_case(1, 8, 2048, 128, "fp8", "bhsd", 31), dict(causal=True, layout="bhsd", softmax_scale=0.125)),
+        (small_case(1, 2, 1000, 128, "fp8", "bshd", 32), dict(causal=True, window_size=(700, -1))),
     ]
+    for inp, kw in cases:
+        kw["descale"] = inp.descale
     if order == "small_then_large":
         cases = cases[::-1]
     for inp, kw in cases:
         q, k, v = _gpu(inp)
-        o = torch.empty_like(q)
+        o = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
         info = plan(q, k, v, o, **kw)
         splits, nbytes = info.splits, info.workspace_bytes
         assert splits > 1 and 0 < nbytes <= 32 << 20, (splits, nbytes)
@@ -51,12 +57,11 @@ def test_noalloc_equals_the_workspace_entry_point(order):
         assert torch.equal(o_na, o_ref) and torch.equal(l_na, l_ref)
     # the last call against the oracle as well
     inp, kw = cases[-1]
-    qf, kf, vf = (stored_f64(t, 1.0) for t in (inp.q, inp.k, inp.v))
+    qf, kf, vf = (stored_f64(t, s) for t, s in zip((inp.q, inp.k, inp.v), inp.descale))
     o_exp, l_exp = oracle.attention(qf, kf, vf, scale=kw.get("softmax_scale", 1.0 / np.sqrt(qf.shape[-1])),
                                     causal=kw["causal"], window=kw.get("window_size", (-1, -1)),
                                     layout=kw.get("layout", "bshd"))
-    kind = "f16" if inp.q.dtype == torch.float16 else "bf16"
-    compare(o_na.float().cpu().double().numpy(), o_exp, l_na.cpu().double().numpy(), l_exp, kind, "noalloc")
+    compare(o_na.float().cpu().double().numpy(), o_exp, l_na.cpu().double().numpy(), l_exp, "fp8", "noalloc")
 
 
 def test_noalloc_without_a_split_and_refusals():
@@ -75,9 +80,19 @@ def test_noalloc_without_a_split_and_refusals():
     a = make_args(q, k, v, o, lse, causal=True)
     a.workspace, a.workspace_bytes = ws.data_ptr(), 4096
     assert _lib.fwd_noalloc(a, torch.cuda.current_stream().cuda_stream) == _lib.EA_EINVAL
+    # a 16-bit launch with few query tiles runs key streams: no scratch either
+    q, k, v = _gpu(small_case(1, 2, 1000, 128, "bf16", "bshd", 34))
+    o = torch.empty_like(q)
+    info = plan(q, k, v, o, causal=True)
+    kernel, splits = info.kernel.decode(), info.splits
+    assert ",ks" in kernel and splits == 1
+    o_ref, l_ref = attention(q, k, v, causal=True)
+    o_na, l_na = _noalloc(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o_na, o_ref) and torch.equal(l_na, l_ref)
     # a split that would need more than the 32 MiB scratch is refused
-    big = torch.zeros(1, 32768, 1, 128, dtype=torch.bfloat16, device="cuda")
-    o = torch.empty_like(big)
+    big = torch.zeros(1, 32768, 1, 128, dtype=torch.float8_e4m3fn, device="cuda")
+    o = torch.empty(big.shape, dtype=torch.bfloat16, device="cuda")
     lse = torch.empty(1, 1, 32768, dtype=torch.float32, device="cuda")
-    a = make_args(big, big, big, o, lse, causal=True)
+    a = make_args(big, big, big, o, lse, causal=True, descale=(1.0, 1.0, 1.0))
     assert _lib.fwd_noalloc(a, torch.cuda.current_stream().cuda_stream) == _lib.EA_ESCRATCH
