@@ -82,8 +82,14 @@ struct Cfg {
 // conflicts.
 __device__ __forceinline__ int v8_swz(int row) { return (row & 3) | (((row >> 3) & 1) << 2); }
 
+// Waves per SIMD: two for 32 rows per wave (256 registers each), one for 64
+// rows per wave or for four key streams (whose LDS holds one workgroup per CU).
+template <int RB, int KS>
+constexpr int kWavesPerEu = (RB == 2 || KS >= 4) ? 1 : 2;
+
 template <In IN, int D, int WAVES, int RB, bool P8, int KS>
-__global__ void __launch_bounds__(64 * WAVES * KS) __attribute__((amdgpu_waves_per_eu(3 - RB, 3 - RB)))
+__global__ void __launch_bounds__(64 * WAVES * KS)
+    __attribute__((amdgpu_waves_per_eu(kWavesPerEu<RB, KS>, kWavesPerEu<RB, KS>)))
 attn_fwd_kernel(const FwdParams p) {
   using C = Cfg<IN, D, WAVES, RB, P8, KS>;
   constexpr In PIN = (IN == In::F16) ? In::F16 : In::BF16;   // type of P, V in LDS and O
@@ -242,17 +248,25 @@ attn_fwd_kernel(const FwdParams p) {
     }
   }
   // Buffer range of tile kt of a K or V head: the tile's first key and the
-  // bytes up to the end of the sequence's last key (0 if kt >= kt_end).  The
-  // resource is built at each load from these plain values; the compiler
-  // shares the scalar work between the loads of a tile.
+  // bytes up to the end of its last key (the sequence's last key in the last
+  // tile; 0 if kt >= kt_end).  The resource is built at each load from these
+  // plain values; the compiler shares the scalar work between the loads of a
+  // tile.  A whole tile's and the last tile's byte counts are fixed per
+  // launch, so a tile costs a select and one 32 x 32 -> 64-bit product (the
+  // host bounds 64 rows of stride below 2^31).
   struct TileRange {
     const unsigned char* base;
     int bytes;
   };
-  auto tile_range = [&](const unsigned char* head, int row_stride, int row_bytes, int kt) {
-    const int k0 = kt * kBN;
-    const int rows = kt < kt_end ? min(n - k0, kBN) : 0;
-    return TileRange{head + (int64_t)k0 * row_stride, rows > 0 ? (rows - 1) * row_stride + row_bytes : 0};
+  const int kt_last = (n - 1) / kBN;
+  const int last_rows = n - kt_last * kBN;
+  const int k_full = (kBN - 1) * k_row_stride + C::kKRow, k_tail = (last_rows - 1) * k_row_stride + C::kKRow;
+  const int v_full = (kBN - 1) * v_row_stride + D * C::kInBytes;
+  const int v_tail = (last_rows - 1) * v_row_stride + D * C::kInBytes;
+  const uint32_t k_tstride = (uint32_t)(kBN * k_row_stride), v_tstride = (uint32_t)(kBN * v_row_stride);
+  auto tile_range = [&](const unsigned char* head, uint32_t tstride, int full, int tail, int kt) {
+    const int bytes = kt >= kt_end ? 0 : (kt < kt_last ? full : tail);
+    return TileRange{head + (uint64_t)(uint32_t)kt * tstride, bytes};
   };
   uint4 vreg[C::kVWiden ? C::kVPer : 1];
   // One load of a tile: K block i, or V item i.
@@ -269,8 +283,8 @@ attn_fwd_kernel(const FwdParams p) {
       load_16b_to_lds(t.base, t.bytes, v_off[i], dst + (wave * kVBlocks + i) * 1024);
     }
   };
-  auto k_range = [&](int kt) { return tile_range(kg, k_row_stride, C::kKRow, kt); };
-  auto v_range = [&](int kt) { return tile_range(vg, v_row_stride, D * C::kInBytes, kt); };
+  auto k_range = [&](int kt) { return tile_range(kg, k_tstride, k_full, k_tail, kt); };
+  auto v_range = [&](int kt) { return tile_range(vg, v_tstride, v_full, v_tail, kt); };
   auto issue_k = [&](int kt, unsigned char* dst) {
     const TileRange t = k_range(kt);
 #pragma unroll
@@ -455,7 +469,7 @@ attn_fwd_kernel(const FwdParams p) {
       for (int r = 0; r < 8; ++r) {
         const float x0 = __builtin_fmaf(s[qb][2 * r], cexp, neg_mc[qb]);
         const float x1 = __builtin_fmaf(s[qb][2 * r + 1], cexp, neg_mc[qb]);
-        x_top[qb] = fmaxf(x_top[qb], fmaxf(x0, x1));
+        x_top[qb] = max3(x_top[qb], x0, x1);
         const float e0 = __builtin_amdgcn_exp2f(x0);
         const float e1 = __builtin_amdgcn_exp2f(x1);
         l_part[qb] += e0;
@@ -577,7 +591,7 @@ attn_fwd_kernel(const FwdParams p) {
           const int r = st * kPairsPerStep + u;
           const float x0 = __builtin_fmaf(sc[qb][2 * r], cexp, neg_mc[qb]);
           const float x1 = __builtin_fmaf(sc[qb][2 * r + 1], cexp, neg_mc[qb]);
-          x_top[qb] = fmaxf(x_top[qb], fmaxf(x0, x1));
+          x_top[qb] = max3(x_top[qb], x0, x1);
           const float e0 = __builtin_amdgcn_exp2f(x0);
           const float e1 = __builtin_amdgcn_exp2f(x1);
           l_part[qb] += e0;
