@@ -17,7 +17,10 @@ visible (unmasked) query/key pairs at 4*d flop each.  ``roofline`` prices the
 kernel's own average duration (HIP events on the launch stream) against the
 MI355X dense MFMA peak of its input type.  ``cpu_baseline`` times the float64
 oracle (the checker of the tests, not a tuned CPU kernel) on a bounded sample
-of the same workload's heads, on the host cores.
+of the same workload's heads, on the host cores.  For the short workloads
+(under 1e11 flop) ``short_sequence`` adds the per-launch time of launches the
+GPU runs back to back (queued behind a spin kernel, so none waits on the
+host's launch path), HBM GB/s from it, and a cold-cache kernel time.
 
 The default workload is the causal bf16 d=128 N=4096 case (B=4, H=32).  The
 warm-up / timed step counts default to the pages' protocol of 10 warm-up calls
@@ -237,6 +240,36 @@ def cold_cache_us(run_once, reps: int = 20, flush_bytes: int = 512 << 20):
     return float(np.median(times))
 
 
+def queued_us(run_once, reps: int = 50):
+    """Per-launch time of `reps` launches that the GPU runs back to back: they
+    are queued behind a spin kernel that lasts longer than the host takes to
+    issue them, so no launch waits on the host (for the short workloads the
+    host's launch path is longer than the kernel)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        run_once()
+    issue_s = time.perf_counter() - t0
+    torch.cuda.synchronize()
+    # cycles of the spin kernel per second of wall time
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    torch.cuda._sleep(1_000_000)
+    b.record(stream)
+    torch.cuda.synchronize()
+    cycles_per_s = 1_000_000 / max(a.elapsed_time(b) * 1e-3, 1e-9)
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(int(3.0 * issue_s * cycles_per_s) + 100_000)
+    s.record(stream)
+    for _ in range(reps):
+        run_once()
+    e.record(stream)
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) * 1e3 / reps
+
+
 def sample_clock(run_once, kernel_ms: float, cap_s: float = 15.0):
     """GFX clock of each XCD and socket power while the kernel runs back to
     back: three `amd-smi metric` samples one second apart, after a second of
@@ -384,7 +417,10 @@ def main(argv=None):
     extra = {}
     if short:
         bytes_ = workload_bytes(w)
+        q_us = queued_us(g["run"])
         extra["short_sequence"] = {
+            "queued_us_per_launch": round(q_us, 2),
+            "queued_algorithmic_GBps": round(bytes_ / (q_us * 1e-6) / 1e9, 1),
             "kernel_us_median": round(g["kernel_ms_median"] * 1e3, 2),
             "kernel_us_min": round(g["kernel_ms_min"] * 1e3, 2),
             "back_to_back_us": round(g["ms_per_step"] * 1e3, 2),

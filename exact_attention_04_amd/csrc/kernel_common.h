@@ -98,18 +98,16 @@ __device__ __forceinline__ float unpack_hi(uint32_t w) {
   else return __builtin_bit_cast(float, w & 0xffff0000u);
 }
 
-// fp8 e4m3 x16 (one uint4) -> bf16 x16 (two uint4), exact.
+// fp8 e4m3 x16 (one uint4) -> bf16 x16 (two uint4), exact (bf16 holds every
+// e4m3 value): one packed convert per two values, bytes 0-1 of a dword to
+// its first bf16 pair and bytes 2-3 to the second, with scale 1.
 __device__ __forceinline__ void fp8x16_to_bf16(uint4 in, uint4& lo, uint4& hi) {
-  uint32_t w[4] = {in.x, in.y, in.z, in.w};
+  const uint32_t w[4] = {in.x, in.y, in.z, in.w};
   uint32_t o[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float a = __builtin_amdgcn_cvt_f32_fp8((int)w[i], 0);
-    const float b = __builtin_amdgcn_cvt_f32_fp8((int)w[i], 1);
-    const float c = __builtin_amdgcn_cvt_f32_fp8((int)w[i], 2);
-    const float d = __builtin_amdgcn_cvt_f32_fp8((int)w[i], 3);
-    o[2 * i] = pack2<In::BF16>(a, b);
-    o[2 * i + 1] = pack2<In::BF16>(c, d);
+    o[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[i], 1.0f, false));
+    o[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[i], 1.0f, true));
   }
   lo = make_uint4(o[0], o[1], o[2], o[3]);
   hi = make_uint4(o[4], o[5], o[6], o[7]);
