@@ -390,43 +390,54 @@ attn_bwd_dkdv_kernel(const BwdParams p) {
   const int qtiles = qt_end - qt_begin;
   const int items = qtiles * p.group;
   float row_val = 0.f;   // lse or D of one query row, staged through a register
-  // the per-row inputs of this batch, read once: inside the loop the fields
-  // would be fetched by vector loads, and a wait for those would also wait
-  // for the tile DMA issued before them
-  const float* const lse_b = p.lse + (int64_t)b * p.lse_sb;
-  const float* const delta_b = p.delta + (int64_t)b * p.delta_sb;
-  const int64_t lse_sh = p.lse_sh, delta_sh = p.delta_sh;
   // The items in order: query head hkv * group + gi, query tile qt (fastest).
+  // A cursor carries its head's Q and dO bases and lse and D rows, so a tile
+  // costs a 32-bit offset (the host bounds a head's rows below 2^32 bytes)
+  // and a select between the whole-tile and last-tile byte counts.
   struct Cursor {
     int gi, qt;
+    const unsigned char* qh;
+    const unsigned char* oh;
+    const float* lh;
+    const float* dh;
+  };
+  auto set_head = [&](Cursor& c) {
+    const int h = hkv * p.group + min(c.gi, p.group - 1);
+    c.qh = (const unsigned char*)p.q + ((int64_t)b * p.q_sb + (int64_t)h * p.q_sh) * 2;
+    c.oh = (const unsigned char*)p.dout + ((int64_t)b * p.do_sb + (int64_t)h * p.do_sh) * 2;
+    c.lh = p.lse + (int64_t)b * p.lse_sb + (int64_t)h * p.lse_sh;
+    c.dh = p.delta + (int64_t)b * p.delta_sb + (int64_t)h * p.delta_sh;
   };
   auto advance = [&](Cursor& c) {
     if (++c.qt == qt_end) {
       c.qt = qt_begin;
       ++c.gi;
+      set_head(c);
     }
   };
-  auto issue = [&](Cursor c, unsigned char* qdst, unsigned char* odst) {
-    const int gi = c.gi, qt = c.qt;
-    const int h = hkv * p.group + gi;
-    const unsigned char* qg = (const unsigned char*)p.q + ((int64_t)b * p.q_sb + (int64_t)h * p.q_sh) * 2;
-    const unsigned char* og = (const unsigned char*)p.dout + ((int64_t)b * p.do_sb + (int64_t)h * p.do_sh) * 2;
-    const Rows64 rq = rows64(qg, q_stride, C::kRow, qt * 64, n);
-    const Rows64 ro = rows64(og, o_stride, C::kRow, qt * 64, n);
+  const int qt_last = (n - 1) / 64;
+  const int q_full = 63 * q_stride + C::kRow, q_tail = (n - 1 - 64 * qt_last) * q_stride + C::kRow;
+  const int o_full = 63 * o_stride + C::kRow, o_tail = (n - 1 - 64 * qt_last) * o_stride + C::kRow;
+  const uint32_t q_tstride = 64u * (uint32_t)q_stride, o_tstride = 64u * (uint32_t)o_stride;
+  // DMA of item c's Q and dO tiles (c.qt < qt_end <= qt_last + 1) and load of
+  // its rows' lse and D values
+  auto issue = [&](const Cursor& c, unsigned char* qdst, unsigned char* odst) {
+    const bool last = c.qt == qt_last;
+    const unsigned char* qbase = c.qh + (uint32_t)c.qt * q_tstride;
+    const unsigned char* obase = c.oh + (uint32_t)c.qt * o_tstride;
+    const int qbytes = last ? q_tail : q_full, obytes = last ? o_tail : o_full;
     // the row value first: its load is then not queued behind the DMA
-    const int r = qt * 64 + (tid & 63);
+    const int r = c.qt * 64 + (tid & 63);
     if (tid < 64) {
-      row_val = r < n ? lse_b[(int64_t)h * lse_sh + r] : INFINITY;
+      row_val = r < n ? c.lh[r] : INFINITY;
     } else if (tid < 128) {
-      row_val = r < n ? delta_b[(int64_t)h * delta_sh + r] : 0.f;
+      row_val = r < n ? c.dh[r] : 0.f;
     }
 #pragma unroll
     for (int i = 0; i < kDma; ++i) {
       // (recomputed per tile: a few VALU instead of registers held across the loop)
-      load_16b_to_lds(rq.base, rq.bytes, dma_offset<C::kRow>(wave * kDma + i, lane, q_stride),
-                      qdst + (wave * kDma + i) * 1024);
-      load_16b_to_lds(ro.base, ro.bytes, dma_offset<C::kRow>(wave * kDma + i, lane, o_stride),
-                      odst + (wave * kDma + i) * 1024);
+      load_16b_to_lds(qbase, qbytes, dma_offset<C::kRow>(wave * kDma + i, lane, q_stride), qdst + (wave * kDma + i) * 1024);
+      load_16b_to_lds(obase, obytes, dma_offset<C::kRow>(wave * kDma + i, lane, o_stride), odst + (wave * kDma + i) * 1024);
     }
   };
   auto commit = [&](int slot) {
@@ -588,20 +599,36 @@ attn_bwd_dkdv_kernel(const BwdParams p) {
   // frees slot (i - 1) % 3 for the next fetch.  Slots are named statically
   // (loop unrolled by three).
   // `nxt`: item i + 1; `cur`: item i.
-  Cursor nxt{0, qt_begin}, cur{0, qt_begin};
-  auto iteration = [&](int i, unsigned char* qa, unsigned char* oa, unsigned char* qb, unsigned char* ob,
-                       unsigned char* qn, unsigned char* on, int sa, int sb, int sn) {
+  // Each role runs its own copy of the loop (roles are fixed per wave), so
+  // the accumulators keep one register assignment throughout; both copies
+  // meet the same barriers.
+  Cursor nxt{0, qt_begin, nullptr, nullptr, nullptr, nullptr};
+  set_head(nxt);
+  Cursor cur = nxt;
+  auto iteration = [&](auto role_tag, int i, unsigned char* qa, unsigned char* oa, unsigned char* qb,
+                       unsigned char* ob, unsigned char* qn, unsigned char* on, int sa, int sb, int sn)
+                       __attribute__((always_inline)) {
     if (i + 1 < items) issue(nxt, qn, on);
     advance(nxt);
-    if (!role_b) {
-      if (i < items) tile_step(BoolTag<false>{}, i & 1, cur.qt * 64, qa, oa, sa);
+    if constexpr (!decltype(role_tag)::value) {
+      if (i < items) tile_step(role_tag, i & 1, cur.qt * 64, qa, oa, sa);
     } else {
-      if (i >= 1) tile_step(BoolTag<true>{}, (i - 1) & 1, 0, ob, qb, sb);
+      if (i >= 1) tile_step(role_tag, (i - 1) & 1, 0, ob, qb, sb);
     }
     advance(cur);
     __builtin_amdgcn_s_waitcnt(0);
     if (i + 1 < items) commit(sn);
     __syncthreads();
+  };
+  auto loop = [&](auto role_tag) __attribute__((always_inline)) {
+    const int total = items + 1;
+    for (int i = 0; i < total; i += 3) {
+      iteration(role_tag, i, qbuf0, obuf0, qbuf2, obuf2, qbuf1, obuf1, 0, 2, 1);
+      if (i + 1 >= total) break;
+      iteration(role_tag, i + 1, qbuf1, obuf1, qbuf0, obuf0, qbuf2, obuf2, 1, 0, 2);
+      if (i + 2 >= total) break;
+      iteration(role_tag, i + 2, qbuf2, obuf2, qbuf1, obuf1, qbuf0, obuf0, 2, 1, 0);
+    }
   };
   if (items > 0) {
     issue(nxt, qbuf0, obuf0);
@@ -609,14 +636,8 @@ attn_bwd_dkdv_kernel(const BwdParams p) {
     __builtin_amdgcn_s_waitcnt(0);
     commit(0);
     __syncthreads();
-    const int total = items + 1;
-    for (int i = 0; i < total; i += 3) {
-      iteration(i, qbuf0, obuf0, qbuf2, obuf2, qbuf1, obuf1, 0, 2, 1);
-      if (i + 1 >= total) break;
-      iteration(i + 1, qbuf1, obuf1, qbuf0, obuf0, qbuf2, obuf2, 1, 0, 2);
-      if (i + 2 >= total) break;
-      iteration(i + 2, qbuf2, obuf2, qbuf1, obuf1, qbuf0, obuf0, 2, 1, 0);
-    }
+    if (role_b) loop(BoolTag<true>{});
+    else loop(BoolTag<false>{});
   }
 
   if (kok) {
