@@ -614,10 +614,17 @@ attn_fwd_kernel(const FwdParams p) {
     }
   };
   // Tiles crossing a mask edge or the sequence end, for this wave's rows.
-  auto tile_masked = [&](int kt) {
-    const int k0 = kt * kBN;
-    return !block_all_visible(wr0, wr1, k0, k0 + kBN, n, p.causal, p.wl, p.wr);
-  };
+  // Each visibility condition is monotone in the tile index, so the tiles
+  // every (row, key) pair of which is visible form one interval [t_lo, t_lo
+  // + t_span): a tile is masked iff it lies outside.
+  int t_hi_key = n - kBN;                                 // last key tile start fully inside the sequence
+  if (p.causal) t_hi_key = min(t_hi_key, wr0 - (kBN - 1));
+  if (p.wr >= 0) t_hi_key = min(t_hi_key, wr0 + p.wr - (kBN - 1));
+  const int t_hi = t_hi_key < 0 ? 0 : t_hi_key / kBN + 1;
+  const int t_lo_key = p.wl >= 0 ? (wr1 - 1) - p.wl : 0;  // first key tile start past the left edge
+  const int t_lo = t_lo_key <= 0 ? 0 : (t_lo_key + kBN - 1) / kBN;
+  const uint32_t t_span = (uint32_t)max(t_hi - t_lo, 0);
+  auto tile_masked = [&](int kt) { return (uint32_t)(kt - t_lo) >= t_span; };
 
   // ---- one 32-key half ("unit") of the software pipeline.  The softmax of
   // the current scores `sc` (tile kt, half hb) runs interleaved with the S
@@ -738,9 +745,18 @@ attn_fwd_kernel(const FwdParams p) {
   // K(i+2) and V(i+1) into the slots freed by the previous iteration, runs
   // the two units, and ends with a barrier once its DMA has landed.
   f32x16 s_a[RB], s_b[RB];
+  // whether some row of the wave still has no reference (wave-uniform); once
+  // every row has one, the per-tile test is skipped
+  bool need_ref = true;
+  auto ref_step = [&]() __attribute__((always_inline)) {
+    if (need_ref) {
+      if (wave_needs_ref()) fold_max(s_a, s_b);
+      need_ref = wave_needs_ref();
+    }
+  };
   auto iter = [&](int kt, const unsigned char* kread, const unsigned char* vread, unsigned char* kwrite,
                   unsigned char* vwrite) __attribute__((always_inline)) {
-    if (wave_needs_ref()) fold_max(s_a, s_b);
+    ref_step();
     const int kt_next = kt + KS;     // this stream's next tile
     const bool m_next = tile_masked(kt_next);
     f32x16 n_a[RB], n_b[RB];
@@ -784,6 +800,7 @@ attn_fwd_kernel(const FwdParams p) {
   };
   auto key_loop = [&]() __attribute__((always_inline)) {
     if (iters <= 0) return;   // no visible key tile (the same in every stream)
+    need_ref = wave_needs_ref();
     issue_k(kt_first_s, kbuf0);
     issue_v(kt_first_s, vbuf0);
     issue_k(kt_first_s + KS, kbuf1);   // zeros if there is no second tile
@@ -813,7 +830,7 @@ attn_fwd_kernel(const FwdParams p) {
     // past the range)
     const unsigned char* vlast = odd ? vbuf1 : vbuf0;
     if (kt < kt_end) {
-      if (wave_needs_ref()) fold_max(s_a, s_b);
+      ref_step();
       if constexpr (P8) {
         float l_tile[RB];
 #pragma unroll
