@@ -233,40 +233,129 @@ attn_bwd_dq_kernel(const BwdParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[0][c][r] = 0.f;
 
-  // one 64-key tile from the slots (kc, vc)
+  // Tiles crossing a mask edge or the sequence end, for this wave's rows:
+  // every visibility condition is monotone in the key tile index, so the
+  // tiles seen in full form one interval [t_lo, t_lo + t_span).
+  int t_hi_key = n - kBN;
+  if (p.causal) t_hi_key = min(t_hi_key, wr0 - (kBN - 1));
+  if (p.wr >= 0) t_hi_key = min(t_hi_key, wr0 + p.wr - (kBN - 1));
+  const int t_hi = t_hi_key < 0 ? 0 : t_hi_key / kBN + 1;
+  const int t_lo_key = p.wl >= 0 ? (wr1 - 1) - p.wl : 0;
+  const int t_lo = t_lo_key <= 0 ? 0 : (t_lo_key + kBN - 1) / kBN;
+  const uint32_t t_span = (uint32_t)max(t_hi - t_lo, 0);
+
+  constexpr int kS = C::kSteps;             // first-product k-steps per half
+  constexpr int kPV = 2 * C::kDBlocks;      // dQ MFMAs per half
+  static_assert(kPV == kS, "one dQ MFMA per first-product step");
+  constexpr int kEPS = 16 / kS;             // dS elements per first-product step
+  constexpr int kLag = 2;                   // steps between an accumulator's last MFMA and its vector work
+  static_assert(kLag <= C::kDBlocks && (kS - kLag) * kEPS >= 8, "lagged vector work");
+  // registers r of a half hold keys 8 (r / 4) + 4 half + r % 4 (of the half)
+  auto mask_half = [&](f32x16& x, int k0) {
+    const int base = k0 + 4 * half - vis_lo;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const uint32_t rel = (uint32_t)(base + 8 * (r >> 2) + (r & 3));
+      if (rel > vis_span) x[r] = -INFINITY;
+    }
+  };
+  // dS^T elements [e0, e0 + cnt) of a half, packed to 16 bits: P = exp2(s c -
+  // lse log2 e) times dP - D
+  auto ds_elems = [&](const f32x16& x, const f32x16& dp, int e0, int cnt, uint32_t (&y)[8]) {
+#pragma unroll
+    for (int e = e0; e < e0 + cnt; e += 2) {
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], cexp, -lse2));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e + 1], cexp, -lse2));
+      y[e / 2] = pack2<IN>(p0 * (dp[e] - delta), p1 * (dp[e + 1] - delta));
+    }
+  };
+  auto row_frag = [&](const unsigned char* tile, int hb, int st) {
+    return *(const uint4*)(tile + 32 * hb * C::kRow + ka[st]);
+  };
+  // K^T fragment of dQ MFMA m of half hb (16 keys j = m / kDBlocks, column block m % kDBlocks)
+  auto tr_frag = [&](const unsigned char* tile, int hb, int m) {
+    const int jj = m / C::kDBlocks, c = m % C::kDBlocks;
+    const unsigned char* base = tile + (32 * hb + 16 * jj) * (2 * D);
+    const uint2 w0 = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + va[0][c])));
+    const uint2 w1 = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + va[1][c])));
+    return make_uint4(w0.x, w0.y, w1.x, w1.y);
+  };
+  auto dq_mfma = [&](uint4 a, const uint32_t (&y)[8], int m) {
+    const int jj = m / C::kDBlocks, c = m % C::kDBlocks;
+    acc[0][c] = mfma_16bit<IN>(a, make_uint4(y[4 * jj], y[4 * jj + 1], y[4 * jj + 2], y[4 * jj + 3]), acc[0][c]);
+  };
+
+  // One 64-key tile from the slots (kc, vc), in four phases so that each
+  // half's vector work runs beside matrix work of the other:
+  //   1. S_a = K_a Q^T, dP_a = V_a dO^T
+  //   2. S_b, dP_b, step by step; half a's dS from step kLag on
+  //   3. dQ^T += K_a^T dS_a^T; the rest of half a's dS first, then half b's
+  //      from step kLag on (the MFMAs that need the last elements of dS_a
+  //      come after step kLag)
+  //   4. dQ^T += K_b^T dS_b^T, after the rest of half b's dS
+  // Row fragments are read two steps ahead of their MFMAs, K^T fragments one
+  // MFMA ahead.  Each step is fenced so the compiler keeps this order.
   auto step = [&](int kt, const unsigned char* kc, const unsigned char* vc) {
-    const bool masked = !block_all_visible(wr0, wr1, kt * kBN, kt * kBN + kBN, n, p.causal, p.wl, p.wr);
+    const bool masked = (uint32_t)(kt - t_lo) >= t_span;
+    f32x16 sa, dpa, sb, dpb;
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      f32x16 s, dp;
+    for (int r = 0; r < 16; ++r) {
+      sa[r] = 0.f; dpa[r] = 0.f; sb[r] = 0.f; dpb[r] = 0.f;
+    }
+    uint32_t ya[8], yb[8];
+    // the row fragments of both halves in order: step i < kS of half a, then of half b
+    auto read_rows = [&](int i, uint4& rk, uint4& rv) {
+      const int hb = i < kS ? 0 : 1, st = i < kS ? i : i - kS;
+      rk = row_frag(kc, hb, st);
+      rv = row_frag(vc, hb, st);
+    };
+    uint4 rk[2], rv[2];
+    read_rows(0, rk[0], rv[0]);
+    read_rows(1, rk[1], rv[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    // 1
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[r] = 0.f;
-        dp[r] = 0.f;
-      }
-      const unsigned char* kb = kc + 32 * hb * C::kRow;
-      const unsigned char* vb = vc + 32 * hb * C::kRow;
+    for (int st = 0; st < kS; ++st) {
+      const uint4 ck = rk[st & 1], cv = rv[st & 1];
+      read_rows(st + 2, rk[st & 1], rv[st & 1]);
+      sa = mfma_16bit<IN>(ck, qf[st], sa);
+      dpa = mfma_16bit<IN>(cv, df[st], dpa);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // 2
+    uint4 ta = make_uint4(0, 0, 0, 0);
 #pragma unroll
-      for (int st = 0; st < C::kSteps; ++st) {
-        s = mfma_16bit<IN>(*(const uint4*)(kb + ka[st]), qf[st], s);
-        dp = mfma_16bit<IN>(*(const uint4*)(vb + ka[st]), df[st], dp);
-      }
-      if (masked) {
-        const int base = kt * kBN + 32 * hb + 4 * half - vis_lo;
+    for (int st = 0; st < kS; ++st) {
+      const uint4 ck = rk[st & 1], cv = rv[st & 1];
+      if (st + 2 < kS) read_rows(kS + st + 2, rk[st & 1], rv[st & 1]);
+      if (st == kS - 1) ta = tr_frag(kc, 0, 0);
+      sb = mfma_16bit<IN>(ck, qf[st], sb);
+      dpb = mfma_16bit<IN>(cv, df[st], dpb);
+      if (st == kLag && masked) mask_half(sa, kt * kBN);
+      if (st >= kLag) ds_elems(sa, dpa, (st - kLag) * kEPS, kEPS, ya);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // 3
+    uint4 tb = make_uint4(0, 0, 0, 0);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const uint32_t rel = (uint32_t)(base + 8 * (r >> 2) + (r & 3));
-          if (rel > vis_span) s[r] = -INFINITY;
-        }
-      }
-      uint32_t pk[1][8];
+    for (int m = 0; m < kPV; ++m) {
+      const uint4 cur = ta;
+      if (m + 1 < kPV) ta = tr_frag(kc, 0, m + 1);
+      else tb = tr_frag(kc, 1, 0);
+      if (m < kLag) ds_elems(sa, dpa, (kS - kLag + m) * kEPS, kEPS, ya);
+      dq_mfma(cur, ya, m);
+      if (m == kLag && masked) mask_half(sb, kt * kBN + 32);
+      if (m >= kLag) ds_elems(sb, dpb, (m - kLag) * kEPS, kEPS, yb);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // 4
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * r], cexp, -lse2));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * r + 1], cexp, -lse2));
-        pk[0][r] = pack2<IN>(p0 * (dp[2 * r] - delta), p1 * (dp[2 * r + 1] - delta));
-      }
-      pv_half<IN, D, 1>(acc, pk, kc, va, hb);   // dQ^T += K^T dS^T
+    for (int m = 0; m < kPV; ++m) {
+      const uint4 cur = tb;
+      if (m + 1 < kPV) tb = tr_frag(kc, 1, m + 1);
+      if (m < kLag) ds_elems(sb, dpb, (kPV - kLag + m) * kEPS, kEPS, yb);
+      dq_mfma(cur, yb, m);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
