@@ -648,10 +648,10 @@ attn_fwd_kernel(const FwdParams p) {
   // operands are ready.
   constexpr int kSMfma = RB * C::kQSteps;            // S MFMAs per half (all row blocks)
   constexpr int kExpValu = RB * 56;                  // softmax VALU per half (all row blocks)
-  // `hook(st)` runs after the S MFMA of k-step st; the first unit of an
-  // iteration uses it to issue the loads of later tiles a few at a time, so
-  // they are spread between the MFMAs rather than issued in one burst, which
-  // would stall the waves that leave a barrier together on the address unit.
+  // `hook(st)` runs after the S MFMA of k-step st; the units of an iteration
+  // use it to issue the loads of later tiles a few at a time, so they are
+  // spread between the MFMAs rather than issued in one burst, which would
+  // stall the waves that leave a barrier together on the address unit.
   // (The scheduler cannot move those loads past LDS reads by itself: they
   // write LDS.)
   auto unit = [&](auto next_tag, f32x16 (&sc)[RB], int hb, const unsigned char* vl, const unsigned char* kn,
@@ -761,16 +761,34 @@ attn_fwd_kernel(const FwdParams p) {
     const bool m_next = tile_masked(kt_next);
     f32x16 n_a[RB], n_b[RB];
     // K of the tile after next (zeros past the last tile) and V of the next,
-    // into the slots the previous iteration freed, spread over the S MFMAs of
-    // the first unit
+    // into the slots the previous iteration freed: K spread over the S MFMAs
+    // of the first unit, V over those of the second (fp8 V that is widened
+    // through registers goes with K, so that it has landed when the
+    // iteration's end converts and stores it)
     const TileRange rk = k_range(kt_next + KS), rv = v_range(kt_next);
-    constexpr int kPer = (kDmaK + kDmaV + C::kQSteps - 1) / C::kQSteps;
+    constexpr int kPerK = (kDmaK + C::kQSteps - 1) / C::kQSteps;
+    constexpr int kPerV = (kDmaV + C::kQSteps - 1) / C::kQSteps;
     auto dma_hook = [&](int st) {
 #pragma unroll
-      for (int u = 0; u < kPer; ++u) {
-        const int i = st * kPer + u;
+      for (int u = 0; u < kPerK; ++u) {
+        const int i = st * kPerK + u;
         if (i < kDmaK) load_k(rk, kwrite, i);
-        else if (i < kDmaK + kDmaV) load_v(rv, vwrite, i - kDmaK);
+      }
+      if constexpr (C::kVWiden) {
+#pragma unroll
+        for (int u = 0; u < kPerV; ++u) {
+          const int i = st * kPerV + u;
+          if (i < kDmaV) load_v(rv, vwrite, i);
+        }
+      }
+    };
+    auto dma_hook_v = [&](int st) {
+      if constexpr (!C::kVWiden) {
+#pragma unroll
+        for (int u = 0; u < kPerV; ++u) {
+          const int i = st * kPerV + u;
+          if (i < kDmaV) load_v(rv, vwrite, i);
+        }
       }
     };
     if constexpr (P8) {
@@ -780,13 +798,13 @@ attn_fwd_kernel(const FwdParams p) {
       uint32_t pa[RB][4], pb[RB][4];
       unit8(BoolTag<true>{}, s_a, 0, kread, n_a, pa, dma_hook);
       if (m_next) apply_mask(n_a, kt_next * kBN, 0);
-      unit8(BoolTag<true>{}, s_b, 1, kread, n_b, pb, [](int) {});
+      unit8(BoolTag<true>{}, s_b, 1, kread, n_b, pb, dma_hook_v);
       if (m_next) apply_mask(n_b, kt_next * kBN, 1);
       tile_pv8(s_a, s_b, pa, pb, l_tile, vread);
     } else {
       unit(BoolTag<true>{}, s_a, 0, vread, kread, n_a, dma_hook);
       if (m_next) apply_mask(n_a, kt_next * kBN, 0);
-      unit(BoolTag<true>{}, s_b, 1, vread, kread, n_b, [](int) {});
+      unit(BoolTag<true>{}, s_b, 1, vread, kread, n_b, dma_hook_v);
       if (m_next) apply_mask(n_b, kt_next * kBN, 1);
     }
 #pragma unroll
