@@ -2,6 +2,7 @@
 // The contract of every entry point is stated in include/ea_attn.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstddef>
 #include <cstdint>
@@ -213,11 +214,42 @@ int validate(const ea_attn_args* a, bool* empty) {
 // they give every CU two workgroups; below that key streams, four streams of
 // 32 rows at d = 64 with fewer than 128 items, else two streams of 128 rows
 // (8 waves, one workgroup per CU: two waves per SIMD).
+// Whether the key work of the 128-row query tiles is unbalanced (causal or
+// windowed masks): the heaviest tile sees at least 1.5x the average key
+// tiles.  O(N / 128) on the host.
+bool unbalanced_tiles(const ea_attn_args* a) {
+  const int n = (int)a->seqlen_q, bm = 128, bn = ea::tile_bn();
+  const int wl = effective_window(a->window_left, n), wr = effective_window(a->window_right, n);
+  const int qt = (n + bm - 1) / bm;
+  int64_t total = 0;
+  int most = 0;
+  for (int t = 0; t < qt; ++t) {
+    const int q0 = t * bm, qlast = std::min(q0 + bm, n) - 1;
+    const int lo = wl >= 0 ? std::max(0, q0 - wl) : 0;
+    int hi = n;
+    if (a->causal) hi = std::min(hi, qlast + 1);
+    if (wr >= 0) hi = std::min(hi, qlast + wr + 1);
+    hi = std::max(lo, hi);
+    const int c = (hi + bn - 1) / bn - lo / bn;
+    total += c;
+    most = std::max(most, c);
+  }
+  return 2 * (int64_t)most * qt >= 3 * total;
+}
+
+// Tile configuration (see plan.cpp): the plain 128-row one when the query
+// tiles fill two workgroups per CU; otherwise key streams: at d = 64, four
+// streams of 32 rows for the fewest tiles, and two streams of 64 rows where
+// the tiles' work is unbalanced (twice the workgroups, so the heaviest-first
+// order balances them); else two streams of 128 rows.
 int choose_cfg(const ea_attn_args* a) {
   if (a->in_dtype == EA_FP8_E4M3) return pv_dtype_of(a) == EA_FP8_E4M3 ? 1 : 0;
   const int64_t items = a->batch * a->nheads_q * ((a->seqlen_q + 127) / 128);
   if (items >= 512) return 0;
-  if (items < 128 && a->headdim == 64) return 3;
+  if (a->headdim == 64) {
+    if (items < 128) return 3;
+    if (unbalanced_tiles(a)) return 4;
+  }
   return 2;
 }
 

@@ -1121,6 +1121,8 @@ static hipError_t launch_16bit(const FwdParams& p, int cfg, hipStream_t stream) 
     case 2: return launch_t<IN, D, 4, 1, false, 2>(p, stream);
     // four streams only at d = 64: four times two K and two V slots must fit a CU's LDS
     case 3: if constexpr (D == 64) return launch_t<IN, D, 1, 1, false, 4>(p, stream); else return hipErrorInvalidValue;
+    // 64 rows and two streams at d = 64 (at d = 128 its registers would leave one wave per SIMD)
+    case 4: if constexpr (D == 64) return launch_t<IN, D, 2, 1, false, 2>(p, stream); else return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 }

@@ -18,13 +18,18 @@ namespace ea {
 //   1: 4 x 1 with the e4m3 P.V (fp8 inputs only);
 //   2: 4 x 2 -- 128 rows, two key streams: 8 waves, one workgroup per CU;
 //   3: 1 x 4 -- 32 rows, four key streams: 4 waves (d = 64 only: four
-//      streams' slots fit a CU's LDS at d = 64).
+//      streams' slots fit a CU's LDS at d = 64);
+//   4: 2 x 2 -- 64 rows, two key streams: 4 waves, two workgroups per CU
+//      (d = 64 only).
 // Streams split a workgroup's key tiles among themselves and merge in LDS.
 // Measured on one MI355X (median kernel time, fp16 d = 64):
 //   B1 H8 N512:           config 0 14.6 us, 2 13.7, 3 10.8 (64 rows x 4: 11.7)
 //   B2 H8 N2048:          config 0 38.0 us, 2 31.1, 3 59.8 (64 rows x 4: 38.6)
 //   B2 H8 N2048 causal:   config 0 (key split) 33.1 us, 2 28.7, 3 44.3
 //                         (64 rows x 4: 27.6)
+// and, in alternated runs on another box, config 4 against the choice above:
+//   B1 H8 N512 11.3 us against 10.7 (config 3); B2 H8 N2048 30.8 against 30.8
+//   (config 2); B2 H8 N2048 causal 24.6 against 27.7 (config 2).
 namespace {
 struct Shape {
   int row_waves, streams;
@@ -33,6 +38,7 @@ Shape shape_of(int cfg) {
   switch (cfg) {
     case 2: return {4, 2};
     case 3: return {1, 4};
+    case 4: return {2, 2};
     default: return {4, 1};
   }
 }
@@ -90,7 +96,7 @@ const char* kernel_name(int in_dtype, int d, int cfg) {
                         sh.streams > 1 ? (sh.streams == 2 ? ",ks2" : ",ks4") : "");
         }
   });
-  if (in_dtype < 1 || in_dtype > 3 || (d != 64 && d != 128) || cfg < 0 || cfg > 3) return "none";
+  if (in_dtype < 1 || in_dtype > 3 || (d != 64 && d != 128) || cfg < 0 || cfg > 4) return "none";
   if (in_dtype == 3 && (d != 128 || cfg > 1)) return "none";
   if (in_dtype != 3 && (cfg == 1 || (cfg > 2 && d != 64))) return "none";
   return names[cfg][d == 128][in_dtype - 1];

@@ -134,15 +134,20 @@ def test_plan_valid_configs():
 
 def test_plan_configuration_by_launch_size():
     # 16-bit: two workgroups of 128 rows per CU (512 items) keep the plain
-    # configuration; fewer items take key streams
-    for (B, N, H, D), name in (((4, 4096, 32, 128), "attn_fwd<bf16,d128,bm128,bn64>"),
-                               ((2, 1024, 32, 128), "attn_fwd<bf16,d128,bm128,bn64>"),
-                               ((2, 1024, 16, 128), "attn_fwd<bf16,d128,bm128,bn64,ks2>"),
-                               ((1, 512, 8, 128), "attn_fwd<bf16,d128,bm128,bn64,ks2>"),
-                               ((2, 2048, 8, 64), "attn_fwd<bf16,d64,bm128,bn64,ks2>"),
-                               ((1, 1920, 8, 64), "attn_fwd<bf16,d64,bm32,bn64,ks4>"),
-                               ((1, 512, 8, 64), "attn_fwd<bf16,d64,bm32,bn64,ks4>")):
-        a = make(B=B, N=N, H=H, D=D, causal=1)
+    # configuration; fewer items take key streams: at d = 64, four streams
+    # of 32 rows for under 128 items, two streams of 64 rows where the
+    # query tiles' key work is unbalanced (causal), else two of 128 rows
+    for (B, N, H, D, causal), name, waves in (
+            ((4, 4096, 32, 128, 1), "attn_fwd<bf16,d128,bm128,bn64>", 4),
+            ((2, 1024, 32, 128, 1), "attn_fwd<bf16,d128,bm128,bn64>", 4),
+            ((2, 1024, 16, 128, 1), "attn_fwd<bf16,d128,bm128,bn64,ks2>", 8),
+            ((1, 512, 8, 128, 1), "attn_fwd<bf16,d128,bm128,bn64,ks2>", 8),
+            ((2, 2048, 8, 64, 1), "attn_fwd<bf16,d64,bm64,bn64,ks2>", 4),
+            ((2, 2048, 8, 64, 0), "attn_fwd<bf16,d64,bm128,bn64,ks2>", 8),
+            ((1, 1920, 8, 64, 1), "attn_fwd<bf16,d64,bm32,bn64,ks4>", 4),
+            ((1, 512, 8, 64, 1), "attn_fwd<bf16,d64,bm32,bn64,ks4>", 4),
+            ((1, 512, 8, 64, 0), "attn_fwd<bf16,d64,bm32,bn64,ks4>", 4)):
+        a = make(B=B, N=N, H=H, D=D, causal=causal)
         for t in "qkvo":
             setattr(a, f"{t}_stride_b", N * H * D)
             setattr(a, f"{t}_stride_s", H * D)
@@ -152,10 +157,21 @@ def test_plan_configuration_by_launch_size():
         a.lse = FAKE + 4 * (B * N * H * D * 2 + 4096)
         a.lse_stride_b, a.lse_stride_h = H * N, N
         st, info = plan_status(a)
-        assert st == 0, ((B, N, H, D), status(st))
-        assert info.kernel.decode() == name, ((B, N, H, D), info.kernel)
-        waves = 8 if "ks2" in name else 4
-        assert info.waves == waves and info.splits == 1 and info.workspace_bytes == 0
+        assert st == 0, ((B, N, H, D, causal), status(st))
+        assert info.kernel.decode() == name, ((B, N, H, D, causal), info.kernel)
+        assert info.waves == waves and info.splits == 1 and info.workspace_bytes == 0, (name, info.waves)
+
+
+def test_plan_window_balance_picks_the_configuration():
+    # at d = 64 with 128-511 items: a window that leaves the query tiles'
+    # key work balanced keeps 128 rows; one that unbalances it takes 64 rows
+    for wl, wr, name in ((200, 200, "attn_fwd<f16,d64,bm128,bn64,ks2>"),
+                         (1500, -1, "attn_fwd<f16,d64,bm128,bn64,ks2>"),
+                         (-1, 0, "attn_fwd<f16,d64,bm64,bn64,ks2>"),
+                         (100, -1, "attn_fwd<f16,d64,bm64,bn64,ks2>")):
+        a = make(B=2, N=2048, H=8, D=64, dtype=_lib.EA_F16, causal=0, window_left=wl, window_right=wr)
+        st, info = plan_status(a)
+        assert st == 0 and info.kernel.decode() == name, (wl, wr, info.kernel)
 
 
 def test_plan_headline_shape():

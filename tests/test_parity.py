@@ -207,6 +207,23 @@ def test_key_streams_uneven_tiles(dtype, d, n, causal, window):
     full_check(inp, dtype, causal=causal, window=window, what=f"streams {dtype} d{d} n{n} {causal} {window}")
 
 
+@pytest.mark.parametrize("n,causal,window", [(700, True, (-1, -1)), (1000, True, (-1, -1)),
+                                             (1500, False, (100, -1)), (1500, False, (-1, 0))])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_two_streams_of_64_rows(dtype, n, causal, window):
+    # d = 64 launches with 128-511 query tiles of 128 rows whose key work is
+    # unbalanced run with 64-row workgroups and two key streams; ragged
+    # tails (N not a multiple of 64) and every kind of mask edge
+    from exact_attention_04_amd import plan
+    from parity_helpers import upload
+    B, H = 4, 8
+    inp = small_case(B, H, n, 64, dtype, "bshd", 9700 + n + (7 if causal else 0))
+    q, k, v = upload(inp)
+    kernel = plan(q, k, v, torch.empty_like(q), causal=causal, window_size=window).kernel.decode()
+    assert "bm64" in kernel and ",ks2" in kernel, kernel
+    full_check(inp, dtype, causal=causal, window=window, what=f"64-row streams {dtype} n{n} {causal} {window}")
+
+
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("scale", [1.0, 2.0])
