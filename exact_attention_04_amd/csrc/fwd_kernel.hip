@@ -581,23 +581,33 @@ attn_fwd_kernel(const FwdParams p) {
 #pragma unroll
     for (int st = 0; st < kSteps; ++st) {
       if (st + kPre < kSteps) a[st + kPre] = *(const uint4*)(kb + ka[st + kPre]);
+      auto softmax_slice = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int qb = 0; qb < RB; ++qb)
+#pragma unroll
+          for (int u = 0; u < kPairsPerStep; ++u) {
+            const int r = st * kPairsPerStep + u;
+            const float x0 = __builtin_fmaf(sc[qb][2 * r], cexp, neg_mc[qb]);
+            const float x1 = __builtin_fmaf(sc[qb][2 * r + 1], cexp, neg_mc[qb]);
+            x_top[qb] = max3(x_top[qb], x0, x1);
+            const float e0 = __builtin_amdgcn_exp2f(x0);
+            const float e1 = __builtin_amdgcn_exp2f(x1);
+            l_part[qb] += e0;
+            l_part[qb] += e1;
+            pk[qb][r] = pack2<PIN>(e0, e1);
+          }
+      };
+      // d = 64 (four steps, two pairs each): the step's softmax slice goes
+      // first, so the K fragment read has that long to land before its MFMA;
+      // at d = 128 the MFMA goes first (measured faster there)
+      if constexpr (D == 64) {
+        softmax_slice();
+        __builtin_amdgcn_sched_barrier(0);
+      }
 #pragma unroll
       for (int qb = 0; qb < RB; ++qb) sn[qb] = mfma_16bit<IN>(a[st], qf[qb][st], sn[qb]);
       hook(st);
-#pragma unroll
-      for (int qb = 0; qb < RB; ++qb)
-#pragma unroll
-        for (int u = 0; u < kPairsPerStep; ++u) {
-          const int r = st * kPairsPerStep + u;
-          const float x0 = __builtin_fmaf(sc[qb][2 * r], cexp, neg_mc[qb]);
-          const float x1 = __builtin_fmaf(sc[qb][2 * r + 1], cexp, neg_mc[qb]);
-          x_top[qb] = max3(x_top[qb], x0, x1);
-          const float e0 = __builtin_amdgcn_exp2f(x0);
-          const float e1 = __builtin_amdgcn_exp2f(x1);
-          l_part[qb] += e0;
-          l_part[qb] += e1;
-          pk[qb][r] = pack2<PIN>(e0, e1);
-        }
+      if constexpr (D != 64) softmax_slice();
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -660,6 +670,14 @@ attn_fwd_kernel(const FwdParams p) {
     float x_top[RB];
 #pragma unroll
     for (int qb = 0; qb < RB; ++qb) x_top[qb] = -INFINITY;
+    // d = 64: the half's V^T fragments are read before its S phase, so they
+    // have landed when its P.V starts (four MFMAs are too few to hide them)
+    constexpr bool kVAhead = D == 64 && !C::kFp8;
+    uint4 vfr[2][kVAhead ? C::kDBlocks : 1];
+    if constexpr (kVAhead) {
+      pv_frags<D>(vfr[0], vl, va, hb, 0);
+      pv_frags<D>(vfr[1], vl, va, hb, 1);
+    }
     if constexpr (decltype(next_tag)::value) {
       // raised priority while the S MFMAs and the softmax interleave: when
       // both waves of a SIMD have work, the one feeding the matrix core from
@@ -687,7 +705,12 @@ attn_fwd_kernel(const FwdParams p) {
 #pragma unroll
     for (int qb = 0; qb < RB; ++qb)
       peak = peak || x_top[qb] > __builtin_amdgcn_logf(pair_sum(l_part[qb])) - kLgPeak;
-    pv_half<PIN, D, RB>(acc, pk, vl, va, hb);
+    if constexpr (kVAhead) {
+      pv_kstep_with<PIN, D, RB>(acc, pk, vfr[0], 0);
+      pv_kstep_with<PIN, D, RB>(acc, pk, vfr[1], 1);
+    } else {
+      pv_half<PIN, D, RB>(acc, pk, vl, va, hb);
+    }
     if (__builtin_amdgcn_ballot_w64(peak) != 0) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {

@@ -219,6 +219,30 @@ __device__ __forceinline__ void pv_kstep(f32x16 (&acc)[RB][D / 32], const uint32
       acc[qb][c] = mfma_16bit<PIN>(aop[c], make_uint4(pk[qb][0], pk[qb][1], pk[qb][2], pk[qb][3]), acc[qb][c]);
 }
 
+// The V^T fragments of one 16-key k-step j of pv_kstep, read ahead of its
+// MFMAs (pv_kstep_with).
+template <int D>
+__device__ __forceinline__ void pv_frags(uint4 (&aop)[D / 32], const unsigned char* vl, const uint32_t (&va)[2][D / 32],
+                                         int hb, int j) {
+  const unsigned char* base = vl + (32 * hb + 16 * j) * (2 * D);
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c) {
+    const uint2 w0 = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + va[0][c])));
+    const uint2 w1 = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + va[1][c])));
+    aop[c] = make_uint4(w0.x, w0.y, w1.x, w1.y);
+  }
+}
+template <In PIN, int D, int RB>
+__device__ __forceinline__ void pv_kstep_with(f32x16 (&acc)[RB][D / 32], const uint32_t (&pk)[RB][8],
+                                              const uint4 (&aop)[D / 32], int j) {
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+    for (int qb = 0; qb < RB; ++qb)
+      acc[qb][c] = mfma_16bit<PIN>(aop[c], make_uint4(pk[qb][4 * j], pk[qb][4 * j + 1], pk[qb][4 * j + 2], pk[qb][4 * j + 3]),
+                                   acc[qb][c]);
+}
+
 // O^T += V^T P^T for both row blocks over the 32 keys [32 hb, 32 hb + 32) of a
 // staged tile, as two k-steps of 16 keys (pv_kstep, j = 0, 1).  P^T (16-bit,
 // B operand) is in the layout the S^T accumulator left it: lane l holds query
