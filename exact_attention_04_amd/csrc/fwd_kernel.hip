@@ -460,16 +460,14 @@ attn_fwd_kernel(const FwdParams p) {
   };
   // p = exp2(x), x = s c - m c, for a 32-key half of every row block, packed
   // to 16 bits; the row sum takes the unrounded fp32 p (the LSE needs it to
-  // fp32 accuracy, which a sum of 16-bit p would miss by up to 2^-9), and
-  // x_top the largest x.
-  auto exp_pack = [&](const f32x16 (&s)[RB], uint32_t (&pk)[RB][8], float (&x_top)[RB]) {
+  // fp32 accuracy, which a sum of 16-bit p would miss by up to 2^-9).
+  auto exp_pack = [&](const f32x16 (&s)[RB], uint32_t (&pk)[RB][8]) {
 #pragma unroll
     for (int qb = 0; qb < RB; ++qb)
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
         const float x0 = __builtin_fmaf(s[qb][2 * r], cexp, neg_mc[qb]);
         const float x1 = __builtin_fmaf(s[qb][2 * r + 1], cexp, neg_mc[qb]);
-        x_top[qb] = max3(x_top[qb], x0, x1);
         const float e0 = __builtin_amdgcn_exp2f(x0);
         const float e1 = __builtin_amdgcn_exp2f(x1);
         l_part[qb] += e0;
@@ -565,7 +563,7 @@ attn_fwd_kernel(const FwdParams p) {
   // Each step is fenced (sched_barrier), so the compiler keeps this order
   // instead of grouping the MFMAs and the vector work apart (16-bit inputs).
   auto s_phase = [&](const unsigned char* kn, int hb, f32x16 (&sn)[RB], const f32x16 (&sc)[RB],
-                     uint32_t (&pk)[RB][8], float (&x_top)[RB], auto&& hook) {
+                     uint32_t (&pk)[RB][8], auto&& hook) {
     constexpr int kSteps = C::kQSteps;
     constexpr int kPre = kSteps < 4 ? kSteps : 4;      // K reads in flight
     constexpr int kPairsPerStep = 8 / kSteps;          // packed P pairs per step
@@ -589,7 +587,6 @@ attn_fwd_kernel(const FwdParams p) {
             const int r = st * kPairsPerStep + u;
             const float x0 = __builtin_fmaf(sc[qb][2 * r], cexp, neg_mc[qb]);
             const float x1 = __builtin_fmaf(sc[qb][2 * r + 1], cexp, neg_mc[qb]);
-            x_top[qb] = max3(x_top[qb], x0, x1);
             const float e0 = __builtin_amdgcn_exp2f(x0);
             const float e1 = __builtin_amdgcn_exp2f(x1);
             l_part[qb] += e0;
@@ -647,15 +644,21 @@ attn_fwd_kernel(const FwdParams p) {
   // not where a few keys hold a large share of a row's weight: a row's first
   // keys, or a peaked row whose dominant keys may sit anywhere in its range.
   // So a half holding a key whose p exceeds 1/kPeak of its row's running sum
-  // (kPeak 8 for bf16 P, 4 for fp16; in the exp2-argument domain,
-  // x > log2(l) - log2(kPeak)) also multiplies the rounding residual
+  // (kPeak 8 for bf16 P, 4 for fp16) also multiplies the rounding residual
   // p - round16(p), itself in 16 bits: P is effectively 16+16 bits there.
   // Every other key carries less than 1/kPeak of its row's final weight,
   // which caps its own rounding error at 2^-11 |v| (bf16) or 2^-13 |v|
-  // (fp16).  The largest x of the half comes from the softmax steps (one max
-  // per pair of scores); the test is wave-uniform (a ballot over the wave's
-  // rows) and its branch follows the main P.V MFMAs, by which time its
-  // operands are ready.
+  // (fp16).  The test runs in two steps, both wave-uniform (ballots over the
+  // wave's rows), after the main P.V MFMAs are issued:
+  //  * a filter: a half whose sum of p over this lane's keys is at most
+  //    1/kPeak of the lane's running sum holds no such key (each p is at most
+  //    that sum, the lane's sum at most the row's); it costs a subtract, a
+  //    multiply and a compare, and passes only a row's first halves and
+  //    halves that add much weight;
+  //  * for halves that pass it, the largest packed p of each lane (16-bit
+  //    values of one sign compare as unsigned integers) against the row's
+  //    running sum, with 2^-7 of slack for the rounding of the packed p, so
+  //    it flags every half the exact p would.
   constexpr int kSMfma = RB * C::kQSteps;            // S MFMAs per half (all row blocks)
   constexpr int kExpValu = RB * 56;                  // softmax VALU per half (all row blocks)
   // `hook(st)` runs after the S MFMA of k-step st; the units of an iteration
@@ -667,9 +670,9 @@ attn_fwd_kernel(const FwdParams p) {
   auto unit = [&](auto next_tag, f32x16 (&sc)[RB], int hb, const unsigned char* vl, const unsigned char* kn,
                   f32x16 (&sn)[RB], auto&& hook) {
     uint32_t pk[RB][8];
-    float x_top[RB];
+    float l_before[RB];   // this lane's row sums before the half
 #pragma unroll
-    for (int qb = 0; qb < RB; ++qb) x_top[qb] = -INFINITY;
+    for (int qb = 0; qb < RB; ++qb) l_before[qb] = l_part[qb];
     // d = 64: the half's V^T fragments are read before its S phase, so they
     // have landed when its P.V starts (four MFMAs are too few to hide them)
     constexpr bool kVAhead = D == 64 && !C::kFp8;
@@ -685,7 +688,7 @@ attn_fwd_kernel(const FwdParams p) {
       __builtin_amdgcn_s_setprio(1);
       if constexpr (C::kFp8) {
         s_half(kn, hb, sn, hook);
-        exp_pack(sc, pk, x_top);
+        exp_pack(sc, pk);
 #pragma unroll
         for (int i = 0; i < kSMfma; ++i) {
           if (i % (4 * RB) == 0) __builtin_amdgcn_sched_group_barrier(0x100, 2 * C::kQSteps, 0);  // K reads
@@ -693,30 +696,43 @@ attn_fwd_kernel(const FwdParams p) {
           __builtin_amdgcn_sched_group_barrier(0x002, kExpValu / kSMfma, 0);                  // softmax VALU
         }
       } else {
-        s_phase(kn, hb, sn, sc, pk, x_top, hook);
+        s_phase(kn, hb, sn, sc, pk, hook);
       }
     } else {
-      exp_pack(sc, pk, x_top);
+      exp_pack(sc, pk);
     }
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(0);
-    constexpr float kLgPeak = (PIN == In::F16) ? 2.f : 3.f;   // log2(kPeak)
-    bool peak = false;
+    constexpr float kPeak = (PIN == In::F16) ? 4.f : 8.f;
+    // pre-filter: the half's share of this lane's sum bounds each of its p
+    bool pre = false;
 #pragma unroll
-    for (int qb = 0; qb < RB; ++qb)
-      peak = peak || x_top[qb] > __builtin_amdgcn_logf(pair_sum(l_part[qb])) - kLgPeak;
+    for (int qb = 0; qb < RB; ++qb) pre = pre || (l_part[qb] - l_before[qb]) * kPeak > l_part[qb];
     if constexpr (kVAhead) {
       pv_kstep_with<PIN, D, RB>(acc, pk, vfr[0], 0);
       pv_kstep_with<PIN, D, RB>(acc, pk, vfr[1], 1);
     } else {
       pv_half<PIN, D, RB>(acc, pk, vl, va, hb);
     }
-    if (__builtin_amdgcn_ballot_w64(peak) != 0) {
+    if (__builtin_amdgcn_ballot_w64(pre) != 0) {
+      bool peak = false;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        uint32_t pr[RB][4];
-        residual(sc, pk, j, pr);
-        pv_kstep<PIN, D, RB>(acc, pr, vl, va, hb, j);
+      for (int qb = 0; qb < RB; ++qb) {
+        typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+        u16x2 m = __builtin_bit_cast(u16x2, pk[qb][0]);
+#pragma unroll
+        for (int r = 1; r < 8; ++r) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, pk[qb][r]));
+        const uint32_t mw = __builtin_bit_cast(uint32_t, m);
+        const float pmax = fmaxf(unpack_lo<PIN>(mw), unpack_hi<PIN>(mw));
+        peak = peak || pmax * (kPeak * 1.0078125f) > pair_sum(l_part[qb]);
+      }
+      if (__builtin_amdgcn_ballot_w64(peak) != 0) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          uint32_t pr[RB][4];
+          residual(sc, pk, j, pr);
+          pv_kstep<PIN, D, RB>(acc, pr, vl, va, hb, j);
+        }
       }
     }
     __builtin_amdgcn_sched_barrier(0);

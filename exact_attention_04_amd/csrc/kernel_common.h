@@ -131,14 +131,6 @@ __device__ __forceinline__ uint4 load_16b(const void* base, int bytes, uint32_t 
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(buffer_rsrc(base, bytes), voff, 0, 0));
 }
 
-// max(a, b, c) in one v_max3_f32.  fmaxf would also quiet signalling NaNs
-// first; the values here come from arithmetic and are never signalling.
-__device__ __forceinline__ float max3(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
-
 // The values of lanes l and l ^ 32 of a wave (the two key halves of one query
 // row), both in every lane: one v_permlane32_swap exchanges the upper 32 lanes
 // of one copy with the lower 32 lanes of the other, so the two results hold
