@@ -461,6 +461,17 @@ attn_bwd_dkdv_kernel(const BwdParams p) {
   const uint32_t qv_span = (uint32_t)(qv_hi - qv_lo);   // (keys past n: never stored)
   const int kw0 = k0 + kw * 32;
   const int kw1 = min(kw0 + 32, n);
+  // 32-row blocks starting at r0 whose rows see every key of this wave's
+  // keys: each visibility condition is monotone in r0, so they form one
+  // interval [vis_r0, vis_r1]
+  int vis_r0 = 0, vis_r1 = 1 << 30;
+  {
+    const int kw1s = kw1 > kw0 ? kw1 : kw0 + 1;
+    if (p.causal) vis_r0 = max(vis_r0, kw1s - 1);
+    if (p.wr >= 0) vis_r0 = max(vis_r0, kw1s - 1 - p.wr);
+    if (p.wl >= 0 && n > kw0 + p.wl + 1) vis_r1 = kw0 + p.wl - 31;
+    if (kw1s > n) vis_r1 = -1;
+  }
 
   const int q_stride = (int)(p.q_ss * 2), o_stride = (int)(p.do_ss * 2);
   uint32_t ka[C::kSteps];
@@ -608,9 +619,8 @@ attn_bwd_dkdv_kernel(const BwdParams p) {
     const uint4* pb = &pbuf[par][kw][0][0];
     bool masked_a = false, masked_b = false;
     if constexpr (!kB) {
-      const int kw1s = kw1 > kw0 ? kw1 : kw0 + 1;
-      masked_a = !block_all_visible(q0, min(q0 + 32, n), kw0, kw1s, n, p.causal, p.wl, p.wr);
-      masked_b = !block_all_visible(q0 + 32, min(q0 + 64, n), kw0, kw1s, n, p.causal, p.wl, p.wr);
+      masked_a = !(q0 >= vis_r0 && q0 <= vis_r1);
+      masked_b = !(q0 + 32 >= vis_r0 && q0 + 32 <= vis_r1);
     }
     // role B's dP accumulators start at -D of their rows (four consecutive
     // registers hold four consecutive rows), so the MFMAs leave dP - D
