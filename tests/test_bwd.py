@@ -181,6 +181,15 @@ def test_bwd_long_sequence(dtype):
     check_bwd(1, 2, 1, 2048, 128, dtype, "causal", "bshd", 4600)
 
 
+@pytest.mark.parametrize("batch,heads", [(1, 8), (2, 8), (4, 8), (5, 8)])
+@pytest.mark.parametrize("mask", ["causal", "none"])
+def test_bwd_head_groups_per_xcd(batch, heads, mask):
+    # (batch, head) counts of 8, 16, 32 and 40: the kernels' work order puts
+    # groups of 1, 2, 4 and 1 heads on each of the 8 XCDs; every workgroup's
+    # unit and head must still be distinct
+    check_bwd(batch, heads, heads, 300, 64, "f16", mask, "bshd", 4700 + batch)
+
+
 def test_bwd_deterministic():
     g = torch.Generator(device="cuda").manual_seed(5)
     q, k, v, do = (torch.randn((2, 1000, 8, 128), device="cuda", generator=g).to(torch.bfloat16) for _ in range(4))
