@@ -132,18 +132,12 @@ __device__ __forceinline__ void store_rows(unsigned char* row_ptr, const f32x16 
 
 }  // namespace
 
-// Work order of a grid of `units` x `heads` workgroups: returns (unit, head)
-// for workgroup w, unit 0 being the heaviest.  Workgroup w runs on XCD w % 8.
-// When the heads split evenly over the XCDs, XCD x takes its heads (8 i + x)
-// in groups of up to four and runs a group's units, heaviest first, before
-// the next group, so the workgroups resident on one XCD read the same few
-// heads' tiles and share them in its L2 (otherwise: unit-major over all
-// heads).
-__device__ __forceinline__ int2 xcd_grouped(int w, int units, int heads) {
+// The backward's work order: groups of up to four heads per XCD (the
+// largest of 4, 2, 1 that splits the heads evenly), else unit-major over
+// all heads.
+__device__ __forceinline__ int2 bwd_order(int w, int units, int heads) {
   if (heads % 8 != 0) return make_int2(w / heads, w % heads);
-  const int g = heads % 32 == 0 ? 4 : heads % 16 == 0 ? 2 : 1;
-  const int x = w & 7, s = w >> 3, per = g * units;
-  return make_int2((s % per) / g, ((s / per) * g + (s % per) % g) * 8 + x);
+  return xcd_grouped(w, units, heads % 32 == 0 ? 4 : heads % 16 == 0 ? 2 : 1);
 }
 
 // ---------------------------------------------------------------------------
@@ -174,7 +168,7 @@ attn_bwd_dq_kernel(const BwdParams p) {
     const int x = bh & 7, y = bh >> 3;
     bh = ((y / p.group) * 8 + x) * p.group + y % p.group;
   } else if (p.group == 1) {
-    const int2 wo = xcd_grouped((int)blockIdx.x, p.q_tiles, bh_count);
+    const int2 wo = bwd_order((int)blockIdx.x, p.q_tiles, bh_count);
     tile = p.q_tiles - 1 - wo.x;
     bh = wo.y;
   }
@@ -445,7 +439,7 @@ attn_bwd_dkdv_kernel(const BwdParams p) {
 
   // key blocks near the start first: under a causal mask they see the most queries
   const int bhk_count = p.batch * p.heads_kv;
-  const int2 wo = xcd_grouped((int)blockIdx.x, p.k_blocks, bhk_count);
+  const int2 wo = bwd_order((int)blockIdx.x, p.k_blocks, bhk_count);
   const int kb = wo.x;
   const int bhk = wo.y;
   const int b = bhk / p.heads_kv;

@@ -130,22 +130,29 @@ attn_fwd_kernel(const FwdParams p) {
   const int col = lane & 31;       // the query row (within each row block) this lane owns
 
   // ---- work assignment: heaviest query tiles first (causal tiles near the
-  // end of the sequence see the most keys), all heads of one tile index
-  // together.  Workgroups go to the 8 XCDs round robin (workgroup w on XCD
-  // w % 8), so with K/V heads shared by groups of query heads the (batch,
-  // head) order is permuted to put each whole group on one XCD, where its
-  // K/V stays in that XCD's L2.
+  // end of the sequence see the most keys).  Workgroups go to the 8 XCDs
+  // round robin (workgroup w on XCD w % 8).  With K/V heads shared by groups
+  // of query heads, all heads of one tile index run together, the (batch,
+  // head) order permuted to put each whole group on one XCD, where its K/V
+  // stays in that XCD's L2; with one K/V head per query head and a head count
+  // that splits into fours per XCD, each XCD runs groups of four heads (all
+  // their tiles) one after the other; otherwise all heads of one tile index
+  // run together.
   // With the keys split (p.splits > 1: too few query tiles to fill the GPU),
   // workgroup item = (query tile, batch and head, key chunk), the chunk index
   // varying fastest.
   const int bh_count = p.batch * p.heads;
   const int chunk = (int)(blockIdx.x % p.splits);
   const int item = (int)(blockIdx.x / p.splits);
-  const int tile = p.q_tiles - 1 - item / bh_count;
+  int tile = p.q_tiles - 1 - item / bh_count;
   int bh = item % bh_count;
   if (p.group > 1 && bh_count % (8 * p.group) == 0) {
     const int x = bh & 7, y = bh >> 3;
     bh = ((y / p.group) * 8 + x) * p.group + y % p.group;
+  } else if (p.group == 1 && p.splits == 1 && bh_count % 32 == 0) {
+    const int2 wo = xcd_grouped(item, p.q_tiles, 4);
+    tile = p.q_tiles - 1 - wo.x;
+    bh = wo.y;
   }
   const int b = bh / p.heads;
   const int h = bh - b * p.heads;

@@ -272,4 +272,15 @@ struct IntTag {
   static constexpr int value = I;
 };
 
+// Work order of a grid of `units` x `heads` workgroups, unit 0 the heaviest:
+// returns (unit, head) of workgroup w.  Workgroups go to the 8 XCDs round
+// robin (w on XCD w % 8); XCD x takes its heads 8 i + x in groups of g and
+// runs a group's units, heaviest first, before the next group, so the
+// workgroups resident on one XCD read the same few heads' tiles through its
+// L2.  The head count must be a multiple of 8 g.
+__device__ __forceinline__ int2 xcd_grouped(int w, int units, int g) {
+  const int x = w & 7, s = w >> 3, per = g * units;
+  return make_int2((s % per) / g, ((s / per) * g + (s % per) % g) * 8 + x);
+}
+
 }  // namespace ea
