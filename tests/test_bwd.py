@@ -91,7 +91,8 @@ def f64(t):
 
 
 def check_bwd(B, H, Hk, N, D, dtype, mask, layout, seed, use_gpu_forward=False):
-    causal, window = MASKS[mask]
+    # mask: a name in MASKS or a (causal, (window_left, window_right)) pair
+    causal, window = MASKS[mask] if isinstance(mask, str) else mask
     inp = small_case(B, H, N, D, dtype, layout, seed, heads_kv=Hk)
     td = torch_dtype(dtype)
     rng = np.random.default_rng(seed + 1)
