@@ -136,9 +136,12 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool
     Returns ``(o, lse)``: o in q's layout and shape (bf16 for fp8 inputs, else
     q's dtype), lse as float32 [B, H, N] (None when ``return_lse`` is False).
     ``descale`` gives the per-tensor fp8 scales (stored value * descale = real
-    value).  ``split_kv`` lets a launch with too few query tiles to fill the
-    GPU split each tile's keys into chunks (a scratch buffer from torch's
-    allocator, merged by a second kernel); False runs it unsplit.
+    value).  ``split_kv`` lets the call use a workspace from torch's
+    allocator, as large as ``plan`` reports: a launch with too few query
+    tiles to fill the GPU splits each tile's keys into chunks (merged by a
+    second kernel), and fp8 inputs with bf16 P.V read a bf16 copy of V
+    widened once by a first kernel (bitwise the same results); False passes
+    no workspace (no split, V widened per tile inside the kernel).
     ``pv_dtype`` (fp8 inputs only): ``torch.float8_e4m3fn`` runs P.V with P
     and V in e4m3 on the 8-bit matrix instructions; None or ``torch.bfloat16``
     keeps P in bf16 (the default).  Raises ValueError for arguments the

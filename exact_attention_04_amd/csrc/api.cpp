@@ -281,6 +281,7 @@ ea::FwdParams make_params(const ea_attn_args* a, int cfg) {
   p.splits = 1;
   p.part_o = nullptr;
   p.part_lse = nullptr;
+  p.v_wide = nullptr;
   return p;
 }
 
@@ -433,6 +434,15 @@ void count_tiles(const ea::FwdParams& p, int cfg, int64_t* tiles, int64_t* maske
   *masked = t_mask * bh;
 }
 
+// Workspace bytes for the bf16 copy of V that fp8 inputs with bf16 P.V read
+// when the caller's workspace holds it (0: no such copy for this call).  The
+// copy's rows are 256 bytes, so it is offered only while a head's rows stay
+// below 2^31 bytes, as the kernels' 32-bit row offsets need.
+int64_t wanted_v_copy(const ea_attn_args* a, int cfg) {
+  if (a->in_dtype != EA_FP8_E4M3 || cfg != 0 || a->seqlen_k >= ((int64_t)1 << 23)) return 0;
+  return ea::widened_v_bytes(a->batch * a->nheads_k, a->seqlen_k, (int)a->headdim);
+}
+
 // Key chunks per query tile this call would use with a large enough workspace,
 // and the workspace that takes.
 int wanted_splits(const ea::FwdParams& p, int cfg, int d, int64_t* bytes) {
@@ -466,11 +476,21 @@ int ea_attn_fwd(const ea_attn_args* args, void* stream) {
   ea::FwdParams p = make_params(args, cfg);
   int64_t need = 0, have = 0;
   const int splits = wanted_splits(p, cfg, (int)args->headdim, &need);
-  void* ws = workspace_of(args, &have);
-  if (splits > 1 && ws != nullptr && have >= need) {
-    p.splits = splits;
-    p.part_o = (float*)ws;
-    p.part_lse = p.part_o + (int64_t)splits * p.batch * p.heads * p.n * args->headdim;
+  const int64_t vcopy = wanted_v_copy(args, cfg);
+  unsigned char* ws = (unsigned char*)workspace_of(args, &have);
+  // The workspace holds [V copy | split partials]; a smaller one serves the
+  // split first (it decides how well a few-tile launch fills the GPU), then
+  // the copy.  Neither changes which values are computed: the copy is exact,
+  // the split only reorders the sums.
+  if (ws != nullptr) {
+    const bool split = splits > 1 && have >= need;
+    const bool copy = vcopy > 0 && have >= vcopy + (split ? need : 0);
+    if (copy) p.v_wide = ws;
+    if (split) {
+      p.splits = splits;
+      p.part_o = (float*)(ws + (copy ? vcopy : 0));
+      p.part_lse = p.part_o + (int64_t)splits * p.batch * p.heads * p.n * args->headdim;
+    }
   }
   e = ea::launch_fwd(p, args->in_dtype, (int)args->headdim, cfg, (hipStream_t)stream);
   if (e != hipSuccess) {
@@ -558,7 +578,7 @@ int ea_attn_plan(const ea_attn_args* args, ea_attn_plan_info* info) {
   if (v2) {
     int64_t need = 0;
     info->splits = wanted_splits(p, cfg, (int)args->headdim, &need);
-    info->workspace_bytes = need;
+    info->workspace_bytes = wanted_v_copy(args, cfg) + need;
   }
   return EA_OK;
 }

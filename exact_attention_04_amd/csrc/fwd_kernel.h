@@ -28,6 +28,11 @@ struct FwdParams {
   int splits;
   float* part_o;
   float* part_lse;
+  // fp8 inputs with P.V in bf16: null, or a [B][Hk][N][D] bf16 buffer that a
+  // first kernel fills with V widened exactly to bf16, which the attention
+  // kernel then loads as it loads 16-bit V (null: each workgroup widens the V
+  // tiles it loads, through registers)
+  void* v_wide;
 };
 
 // Split of the keys for a launch of `items` query tiles x heads whose tiles
@@ -36,6 +41,9 @@ struct FwdParams {
 int choose_splits(int64_t items, int max_kv_tiles, int64_t total_kv_tiles);
 // Workspace bytes for `splits` chunks (0 for one).
 int64_t split_workspace_bytes(int splits, int64_t batch_heads, int64_t n, int d);
+// Bytes of the widened bf16 copy of an fp8 V (FwdParams::v_wide), rounded up
+// to 256 so that what follows it in a workspace stays aligned.
+int64_t widened_v_bytes(int64_t batch_heads_kv, int64_t n, int d);
 
 // The allocation-free entry point's scratch: a static device array of
 // kScratchBytes per GPU holding the key split's partial results (in place of
@@ -47,7 +55,9 @@ hipError_t scratch_address(int dev, void** ptr);
 
 // Kernel configurations (64 keys per K/V tile, 32 query rows per wave):
 //   0: 128 rows per workgroup (4 waves), P.V in 16 bits (fp8 V widened
-//      exactly to bf16); two workgroups per CU, two waves per SIMD;
+//      exactly to bf16, by a first kernel into FwdParams::v_wide when that
+//      is set, else per tile in the attention kernel); two workgroups per
+//      CU, two waves per SIMD;
 //   1: as 0 for fp8 inputs with P and V in e4m3 on the 8-bit instruction;
 //   2, 3 (16-bit inputs): the workgroup's waves form key streams that split
 //      the key tiles and merge in LDS, for launches with few query tiles:

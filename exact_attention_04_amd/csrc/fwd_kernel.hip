@@ -52,17 +52,20 @@
 
 namespace ea {
 
-template <In IN, int D, int WAVES, int RB, bool P8, int KS>
+// V16: fp8 inputs whose V arrives already widened to bf16 (FwdParams::v_wide).
+template <In IN, int D, int WAVES, int RB, bool P8, int KS, bool V16>
 struct Cfg {
   static constexpr bool kFp8 = (IN == In::FP8);
   static_assert(!P8 || (kFp8 && D == 128), "e4m3 P.V: fp8 inputs, d = 128");
   static_assert(KS == 1 || !kFp8, "key streams: 16-bit inputs");
+  static_assert(!V16 || (kFp8 && !P8), "a widened V copy: fp8 inputs, bf16 P.V");
   static constexpr int kThreads = 64 * WAVES;                 // one key stream's threads
   static constexpr int kBM = 32 * RB * WAVES;        // query rows per workgroup
   static constexpr int kInBytes = kFp8 ? 1 : 2;
   static constexpr int kKRow = D * kInBytes;         // bytes per K row in LDS
   static constexpr int kVRow = P8 ? D : D * 2;       // V in LDS: e4m3 for P8, else 16-bit
-  static constexpr bool kVWiden = kFp8 && !P8;       // fp8 V widened to bf16 through registers
+  static constexpr bool kVWiden = kFp8 && !P8 && !V16;   // fp8 V widened to bf16 through registers
+  static constexpr int kVInBytes = V16 ? 2 : kInBytes;   // bytes per V element in global memory
   static constexpr int kKTile = kBN * kKRow;
   static constexpr int kVTile = kBN * kVRow;
   static constexpr int kStage = kKTile + kVTile;
@@ -87,11 +90,11 @@ __device__ __forceinline__ int v8_swz(int row) { return (row & 3) | (((row >> 3)
 template <int RB, int KS>
 constexpr int kWavesPerEu = (RB == 2 || KS >= 4) ? 1 : 2;
 
-template <In IN, int D, int WAVES, int RB, bool P8, int KS>
+template <In IN, int D, int WAVES, int RB, bool P8, int KS, bool V16>
 __global__ void __launch_bounds__(64 * WAVES * KS)
     __attribute__((amdgpu_waves_per_eu(kWavesPerEu<RB, KS>, kWavesPerEu<RB, KS>)))
 attn_fwd_kernel(const FwdParams p) {
-  using C = Cfg<IN, D, WAVES, RB, P8, KS>;
+  using C = Cfg<IN, D, WAVES, RB, P8, KS, V16>;
   constexpr In PIN = (IN == In::F16) ? In::F16 : In::BF16;   // type of P, V in LDS and O
   constexpr int kBM = C::kBM;
   // LDS: two K slots and two V slots.  K of tile i+1 and V of tile i are
@@ -162,9 +165,9 @@ attn_fwd_kernel(const FwdParams p) {
 
   const unsigned char* qg = (const unsigned char*)p.q + ((int64_t)b * p.q_sb + (int64_t)h * p.q_sh) * C::kInBytes;
   const unsigned char* kg = (const unsigned char*)p.k + ((int64_t)b * p.k_sb + (int64_t)hkv * p.k_sh) * C::kInBytes;
-  const unsigned char* vg = (const unsigned char*)p.v + ((int64_t)b * p.v_sb + (int64_t)hkv * p.v_sh) * C::kInBytes;
+  const unsigned char* vg = (const unsigned char*)p.v + ((int64_t)b * p.v_sb + (int64_t)hkv * p.v_sh) * C::kVInBytes;
   const int k_row_stride = (int)(p.k_ss * C::kInBytes);   // bytes; < 2^31 (checked by the host)
-  const int v_row_stride = (int)(p.v_ss * C::kInBytes);
+  const int v_row_stride = (int)(p.v_ss * C::kVInBytes);
 
   const KeyRange kr = tile_key_range(q0, kBM, n, p.causal, p.wl, p.wr);
   // this workgroup's key tiles: chunk `chunk` of p.splits contiguous chunks
@@ -268,8 +271,8 @@ attn_fwd_kernel(const FwdParams p) {
   const int kt_last = (n - 1) / kBN;
   const int last_rows = n - kt_last * kBN;
   const int k_full = (kBN - 1) * k_row_stride + C::kKRow, k_tail = (last_rows - 1) * k_row_stride + C::kKRow;
-  const int v_full = (kBN - 1) * v_row_stride + D * C::kInBytes;
-  const int v_tail = (last_rows - 1) * v_row_stride + D * C::kInBytes;
+  const int v_full = (kBN - 1) * v_row_stride + D * C::kVInBytes;
+  const int v_tail = (last_rows - 1) * v_row_stride + D * C::kVInBytes;
   const uint32_t k_tstride = (uint32_t)(kBN * k_row_stride), v_tstride = (uint32_t)(kBN * v_row_stride);
   auto tile_range = [&](const unsigned char* head, uint32_t tstride, int full, int tail, int kt) {
     const int bytes = kt >= kt_end ? 0 : (kt < kt_last ? full : tail);
@@ -1144,11 +1147,11 @@ hipError_t scratch_address(int dev, void** ptr) {
   return status[dev];
 }
 
-template <In IN, int D, int WAVES, int RB, bool P8, int KS>
+template <In IN, int D, int WAVES, int RB, bool P8, int KS, bool V16 = false>
 static hipError_t launch_t(const FwdParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)((int64_t)p.q_tiles * p.batch * p.heads * p.splits));
   const dim3 block(64 * WAVES * KS);
-  hipLaunchKernelGGL((attn_fwd_kernel<IN, D, WAVES, RB, P8, KS>), grid, block, 0, stream, p);
+  hipLaunchKernelGGL((attn_fwd_kernel<IN, D, WAVES, RB, P8, KS, V16>), grid, block, 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
   constexpr In OUT = (IN == In::F16) ? In::F16 : In::BF16;
@@ -1173,10 +1176,48 @@ static hipError_t launch_16bit(const FwdParams& p, int cfg, hipStream_t stream) 
   }
 }
 
+// fp8 V widened exactly to bf16 (every e4m3 value is a bf16 value) into
+// the copy [B][Hk][N][D]: one thread per 16 stored bytes of a V row.  It is
+// bound by HBM (one byte read and two written per element), and lets the
+// attention kernel load bf16 V tiles by DMA, as for 16-bit inputs, instead
+// of every workgroup widening each V tile it loads through its registers.
+template <int D>
+__global__ void __launch_bounds__(256) attn_widen_v(const FwdParams p) {
+  constexpr int kChunks = D / 16;
+  const int hk = p.heads / p.group;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= (int64_t)p.batch * hk * p.n * kChunks) return;
+  const int c = (int)(t % kChunks);
+  const int64_t r = t / kChunks;                 // copy row: (b Hk + h) N + s
+  const int s = (int)(r % p.n);
+  const int64_t bh = r / p.n;
+  const int h = (int)(bh % hk), b = (int)(bh / hk);
+  const unsigned char* src =
+      (const unsigned char*)p.v + (int64_t)b * p.v_sb + (int64_t)h * p.v_sh + (int64_t)s * p.v_ss + c * 16;
+  uint4 lo, hi;
+  fp8x16_to_bf16(*(const uint4*)src, lo, hi);
+  uint4* dst = (uint4*)((unsigned char*)p.v_wide + (r * D + c * 16) * 2);
+  dst[0] = lo;
+  dst[1] = hi;
+}
+
 hipError_t launch_fwd(const FwdParams& p, int in_dtype, int d, int cfg, hipStream_t stream) {
   // in_dtype: 1 = f16, 2 = bf16, 3 = fp8 e4m3 (validated by the caller)
   if (in_dtype == 3) {
     if (d != 128) return hipErrorInvalidValue;
+    if (cfg == 0 && p.v_wide != nullptr) {
+      const int64_t threads = (int64_t)p.batch * (p.heads / p.group) * p.n * (128 / 16);
+      hipLaunchKernelGGL((attn_widen_v<128>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, p);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      // the attention kernel reads the copy: element strides of [B][Hk][N][D]
+      FwdParams pw = p;
+      pw.v = p.v_wide;
+      pw.v_ss = 128;
+      pw.v_sh = (int64_t)p.n * 128;
+      pw.v_sb = (int64_t)(p.heads / p.group) * p.n * 128;
+      return launch_t<In::FP8, 128, 4, 1, false, 1, true>(pw, stream);
+    }
     if (cfg == 0) return launch_t<In::FP8, 128, 4, 1, false, 1>(p, stream);
     if (cfg == 1) return launch_t<In::FP8, 128, 4, 1, true, 1>(p, stream);
     return hipErrorInvalidValue;

@@ -69,6 +69,10 @@ int choose_splits(int64_t items, int max_kv_tiles, int64_t total_kv_tiles) {
 int64_t split_workspace_bytes(int splits, int64_t batch_heads, int64_t n, int d) {
   return splits > 1 ? (int64_t)splits * batch_heads * n * (d + 1) * 4 : 0;
 }
+
+int64_t widened_v_bytes(int64_t batch_heads_kv, int64_t n, int d) {
+  return (batch_heads_kv * n * d * 2 + 255) / 256 * 256;
+}
 int tile_waves(int cfg) { return shape_of(cfg).row_waves * shape_of(cfg).streams; }
 int tile_bn() { return kBN; }
 

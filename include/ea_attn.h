@@ -101,13 +101,21 @@ typedef struct ea_attn_args {
   int64_t v_stride_b, v_stride_s, v_stride_h;
   int64_t o_stride_b, o_stride_s, o_stride_h;
   int64_t lse_stride_b, lse_stride_h;   /* LSE rows are contiguous along Nq */
-  /* Optional scratch for launches with too few query tiles to fill the GPU
-     (ea_attn_plan reports the bytes wanted, 0 if none): the keys of each tile
-     are then split into chunks whose partial results are merged by a second
-     kernel.  NULL, or fewer bytes than wanted, runs without the split (same
-     results up to rounding).  Device memory, 16-byte aligned, owned by the
-     caller; its contents need no initialisation and are overwritten; launches
-     that may run at the same time need separate workspaces. */
+  /* Optional scratch (ea_attn_plan reports the bytes wanted, 0 if none),
+     laid out as [V copy | split partials]:
+     - fp8 inputs with P.V in bf16: a bf16 copy of V, B x Hk x Nk x D x 2
+       bytes rounded up to 256, which a first kernel fills with V widened
+       exactly to bf16; the attention kernel then loads V as for 16-bit
+       inputs instead of widening each V tile it loads.  Results are
+       bitwise the same with or without it.
+     - launches with too few query tiles to fill the GPU: the keys of each
+       tile are split into chunks whose partial results are merged by a
+       second kernel (same results up to rounding).
+     NULL runs with neither; fewer bytes than wanted serve the split first
+     (when they hold its part), then the copy (when they hold it as well).
+     Device memory, 16-byte aligned, owned by the caller; its contents need
+     no initialisation and are overwritten; launches that may run at the same
+     time need separate workspaces. */
   void* workspace;
   int64_t workspace_bytes;
   /* Number format of P and V in the P.V product, for fp8 inputs ("Flash
@@ -136,7 +144,8 @@ typedef struct ea_attn_plan_info {
   int64_t kv_tiles;          /* K/V tiles visited over the whole launch */
   int64_t masked_tiles;      /* of which need per-element masking */
   char kernel[64];           /* name of the kernel instantiation */
-  int64_t workspace_bytes;   /* ea_attn_args.workspace size that enables the key split */
+  int64_t workspace_bytes;   /* ea_attn_args.workspace size that enables the key split
+                                and, for fp8 inputs with bf16 P.V, the copy of V */
   int32_t splits;            /* key chunks per query tile with that workspace (1: none) */
   int32_t reserved;
 } ea_attn_plan_info;
@@ -178,11 +187,13 @@ int ea_attn_fwd(const ea_attn_args* args, void* stream);
  * args->workspace must be NULL: a launch that splits its keys (the plan's
  * splits > 1) keeps the partial results in a static device array of the
  * library, 32 MiB per GPU, which each GPU the library runs on holds until the
- * process ends.  Nothing is allocated, freed or copied by this call.
+ * process ends; fp8 inputs with bf16 P.V widen V per tile inside the kernel
+ * (no copy of V).  Nothing is allocated, freed or copied by this call.
  *   EA_EINVAL        as ea_attn_fwd, and a non-NULL workspace.
- *   EA_ESCRATCH      the plan's workspace_bytes exceeds 32 MiB (checked
- *                    before any device call; ea_attn_fwd with a caller
- *                    workspace, or with none, runs such a problem).
+ *   EA_ESCRATCH      the key split's partial results (the plan's
+ *                    workspace_bytes less the fp8 V copy) exceed 32 MiB
+ *                    (checked before any device call; ea_attn_fwd with a
+ *                    caller workspace, or with none, runs such a problem).
  *   EA_EUNSUPPORTED, EA_EDEVICE, EA_EHIP   as ea_attn_fwd.
  * All calls on one GPU share that GPU's array, and it keeps the last call's
  * contents (every element a launch reads, it first writes, so nothing needs

@@ -259,14 +259,22 @@ def test_key_split_plan_and_workspace_rules():
     # workgroup (key streams): no workspace
     st, info = plan_status(make(B=2, N=2048, H=8, D=64, dtype=_lib.EA_F16, causal=1))
     assert st == 0 and info.splits == 1 and info.workspace_bytes == 0 and "ks2" in info.kernel.decode()
-    # fp8: balanced work (no mask) is not split, however few the query tiles
+    # fp8: balanced work (no mask) is not split, however few the query tiles;
+    # with P.V in bf16 the workspace wanted is the bf16 copy of V
+    # (B x Hk x N x D x 2 bytes), with e4m3 P.V nothing
     st, info = plan_status(make(B=1, N=512, H=8, D=128, dtype=fp8))
+    assert st == 0 and info.splits == 1 and info.workspace_bytes == 8 * 512 * 128 * 2
+    st, info = plan_status(make(B=1, N=512, H=8, D=128, dtype=fp8, pv_dtype=fp8))
     assert st == 0 and info.splits == 1 and info.workspace_bytes == 0
+    # shared K/V heads: the copy holds the K/V heads only
+    st, info = plan_status(make(B=2, N=100, H=8, D=128, dtype=fp8, nheads_k=2))
+    assert st == 0 and info.workspace_bytes == (2 * 2 * 100 * 128 * 2 + 255) // 256 * 256
     # causal fp8 B1 H8 N2048: 128 items, the heaviest tile sees 32 key tiles
-    # against 17 on average -> 2 chunks
+    # against 17 on average -> 2 chunks; the workspace holds the copy of V,
+    # then the chunks' partial results
     st, info = plan_status(make(B=1, N=2048, H=8, D=128, dtype=fp8, causal=1))
     assert st == 0 and info.splits == 2
-    assert info.workspace_bytes == 2 * 8 * 2048 * (128 + 1) * 4
+    assert info.workspace_bytes == 8 * 2048 * 128 * 2 + 2 * 8 * 2048 * (128 + 1) * 4
     # causal fp8 B1 H2 N1000: 16 items -> up to 8 chunks, capped by the balance rule
     st, info = plan_status(make(B=1, N=1000, H=2, D=128, causal=1, dtype=fp8))
     assert st == 0 and info.splits == 2
@@ -462,7 +470,8 @@ def test_noalloc_scratch_limit_and_workspace_rules():
     a = make(B=1, N=32768, H=1, D=128, causal=1, dtype=_lib.EA_FP8_E4M3)
     st, info = plan_status(a)
     assert st == 0 and info.splits == 2
-    assert info.workspace_bytes == 2 * 32768 * 129 * 4 > 32 << 20
+    assert info.workspace_bytes == 32768 * 128 * 2 + 2 * 32768 * 129 * 4   # V copy + split
+    assert 2 * 32768 * 129 * 4 > 32 << 20
     assert abi().ea_attn_fwd_noalloc(ctypes.byref(a), None) == _lib.EA_ESCRATCH
     assert "scratch" in status(_lib.EA_ESCRATCH)
     with pytest.raises(ValueError):

@@ -135,8 +135,9 @@ def test_no_device_allocation():
     torch.cuda.synchronize()
     assert torch.cuda.max_memory_allocated() == before
     # with the key split among workgroups (fp8, 64 query tiles x heads here)
-    # the only extra memory is the planned scratch: chunks x B x H x N x
-    # (D + 1) float32, linear in N
+    # the only extra memory is the planned workspace: the bf16 copy of V
+    # (B x Hk x N x D x 2 bytes), then chunks x B x H x N x (D + 1) float32,
+    # both linear in N
     inp8 = small_case(2, 4, 1024, 128, "fp8", "bshd", 5)
     q8, k8, v8 = _gpu(inp8)
     o8 = torch.empty(q8.shape, dtype=torch.bfloat16, device="cuda")
