@@ -134,13 +134,14 @@ attn_fwd_kernel(const FwdParams p) {
 
   // ---- work assignment: heaviest query tiles first (causal tiles near the
   // end of the sequence see the most keys).  Workgroups go to the 8 XCDs
-  // round robin (workgroup w on XCD w % 8).  With K/V heads shared by groups
-  // of query heads, all heads of one tile index run together, the (batch,
-  // head) order permuted to put each whole group on one XCD, where its K/V
-  // stays in that XCD's L2; with one K/V head per query head and a head count
-  // that splits into fours per XCD, each XCD runs groups of four heads (all
-  // their tiles) one after the other; otherwise all heads of one tile index
-  // run together.
+  // round robin (workgroup w on XCD w % 8), each with its own L2.  Each XCD
+  // runs a few K/V heads' work at a time (all their query tiles, heaviest
+  // first, then the next few), so its resident workgroups share those heads'
+  // K/V in its L2: four heads without shared K/V heads, the query heads of
+  // two K/V heads (one if the K/V head count only splits into eights) with
+  // them.  Where the heads do not split evenly over the XCDs, all heads of
+  // one tile index run together (with shared K/V heads, the (batch, head)
+  // order permuted to put each whole group on one XCD).
   // With the keys split (p.splits > 1: too few query tiles to fill the GPU),
   // workgroup item = (query tile, batch and head, key chunk), the chunk index
   // varying fastest.
@@ -149,7 +150,13 @@ attn_fwd_kernel(const FwdParams p) {
   const int item = (int)(blockIdx.x / p.splits);
   int tile = p.q_tiles - 1 - item / bh_count;
   int bh = item % bh_count;
-  if (p.group > 1 && bh_count % (8 * p.group) == 0) {
+  const int bhk_count = bh_count / p.group;
+  if (p.group > 1 && p.splits == 1 && bhk_count % 8 == 0) {
+    // units of a K/V head: (tile, query head of its group), the tile slowest
+    const int2 wo = xcd_grouped(item, p.q_tiles * p.group, bhk_count % 16 == 0 ? 2 : 1);
+    tile = p.q_tiles - 1 - wo.x / p.group;
+    bh = wo.y * p.group + wo.x % p.group;
+  } else if (p.group > 1 && bh_count % (8 * p.group) == 0) {
     const int x = bh & 7, y = bh >> 3;
     bh = ((y / p.group) * 8 + x) * p.group + y % p.group;
   } else if (p.group == 1 && p.splits == 1 && bh_count % 32 == 0) {

@@ -277,7 +277,9 @@ struct IntTag {
 // robin (w on XCD w % 8); XCD x takes its heads 8 i + x in groups of g and
 // runs a group's units, heaviest first, before the next group, so the
 // workgroups resident on one XCD read the same few heads' tiles through its
-// L2.  The head count must be a multiple of 8 g.
+// L2.  The head count must be a multiple of 8 g.  A unit is whatever the
+// caller makes of it (a query tile; a query tile of one of a K/V head's
+// query heads).
 __device__ __forceinline__ int2 xcd_grouped(int w, int units, int g) {
   const int x = w & 7, s = w >> 3, per = g * units;
   return make_int2((s % per) / g, ((s / per) * g + (s % per) % g) * 8 + x);

@@ -104,6 +104,21 @@ def test_shared_kv_heads(heads, heads_kv, mask, layout):
                what=f"H{heads}/Hk{heads_kv} {mask} {layout}")
 
 
+@pytest.mark.parametrize("batch,heads,heads_kv", [(1, 64, 8), (2, 64, 8), (1, 72, 24), (2, 32, 4)])
+def test_shared_kv_heads_xcd_groups(batch, heads, heads_kv):
+    # (batch, K/V head) counts of 8, 16, 24 and 8: the work order puts the
+    # query heads of one K/V head (8, 24) or of two (16) on an XCD at a time;
+    # at least 512 query tiles x heads (N = 1100), so the plain configuration
+    # runs
+    from exact_attention_04_amd import plan
+    from parity_helpers import upload
+    inp = small_case(batch, heads, 1100, 128, "bf16", "bshd", 9900 + batch * 10 + heads_kv, heads_kv=heads_kv)
+    q, k, v = upload(inp)
+    info = plan(q, k, v, torch.empty_like(q), causal=True)
+    assert ",ks" not in info.kernel.decode() and info.splits == 1, info.kernel
+    full_check(inp, "bf16", causal=True, what=f"xcd groups B{batch} H{heads}/Hk{heads_kv}")
+
+
 @pytest.mark.parametrize("dtype,d", [("f16", 64), ("fp8", 128)])
 def test_shared_kv_heads_other_types(dtype, d):
     inp = small_case(1, 8, 300, d, dtype, "bshd", 71, heads_kv=2)
