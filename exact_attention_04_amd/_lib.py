@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libea_attn.so")
 
 EA_OK, EA_EINVAL, EA_EUNSUPPORTED, EA_EDEVICE, EA_EHIP, EA_ESCRATCH = 0, 1, 2, 3, 4, 5
 EA_F16, EA_BF16, EA_FP8_E4M3, EA_F32 = 1, 2, 3, 4
-EA_ABI_VERSION = 4
+EA_ABI_VERSION = 5
 
 # Every symbol the header declares.
 EXPORTS = ("ea_attn_fwd", "ea_attn_fwd_noalloc", "ea_attn_bwd", "ea_attn_plan", "ea_status_string",

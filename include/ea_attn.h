@@ -35,7 +35,9 @@
 extern "C" {
 #endif
 
-#define EA_ABI_VERSION 4u
+/* 5: the forward's workspace may also hold the bf16 copy of an fp8 V, and
+   ea_attn_plan's workspace_bytes includes it (no struct changed). */
+#define EA_ABI_VERSION 5u
 
 /* Status codes. */
 enum ea_status {
