@@ -46,8 +46,9 @@ METRIC = "attention fwd TFLOP/s and % of MFMA peak (bf16 causal d=128, N=4096)"
 # MI355X dense MFMA peaks (256 CUs x 2.4 GHz): 16-bit 4096 flop/CU/clk, fp8 8192.
 PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "fp8": 5033.2}
 HBM_PEAK_GBS = 8000.0
-# the forward kernel's sources (a recorded traffic measurement is valid only for these)
+# the forward and backward kernels' sources (a recorded traffic measurement is valid only for these)
 KERNEL_SRCS = [os.path.join(ROOT, "exact_attention_04_amd", "csrc", f) for f in ("fwd_kernel.hip", "kernel_common.h")]
+BWD_KERNEL_SRCS = [os.path.join(ROOT, "exact_attention_04_amd", "csrc", f) for f in ("bwd_kernel.hip", "kernel_common.h")]
 
 
 def visible_pairs_per_head(w) -> int:
@@ -82,22 +83,24 @@ def kernel_code(text: str) -> str:
     return "\n".join(line for line in lines if line.strip())
 
 
-def kernel_hash() -> str:
+def kernel_hash(srcs=None) -> str:
     h = hashlib.sha256()
-    for path in KERNEL_SRCS:
+    for path in srcs or KERNEL_SRCS:
         with open(path, encoding="utf-8") as f:
             h.update(kernel_code(f.read()).encode())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str, pv8: bool = False):
-    """HBM bytes per launch from a committed counter summary, if still current."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}{'_pv8' if pv8 else ''}.json")
+def measured_traffic(workload: str, pv8: bool = False, bwd: bool = False):
+    """HBM bytes per launch (per backward call with `bwd`) from a committed
+    counter summary, if still current."""
+    name = f"traffic_bwd_{workload}" if bwd else f"traffic_{workload}{'_pv8' if pv8 else ''}"
+    path = os.path.join(ROOT, "profiles", name + ".json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_sha256_16") != kernel_hash():
+    if rec.get("kernel_sha256_16") != kernel_hash(BWD_KERNEL_SRCS if bwd else None):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -485,6 +488,8 @@ def main_bwd(args, name, w):
     """One JSON line for the backward pass on workload `w` (16-bit inputs)."""
     flops = 2.5 * workload_flops(w)   # five products of the forward's size: S, dP, dV, dK, dQ
     g = time_gpu_bwd(w, args.steps, args.warmup)
+    if args.copy_calibration:
+        copy_calibration()
     achieved = flops / (g["kernel_ms_avg"] * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     esz = 2
@@ -501,7 +506,7 @@ def main_bwd(args, name, w):
                    "seqlen": w.seqlen, "headdim": w.headdim, "causal": w.causal,
                    "window": [w.window_left, w.window_right], "layout": w.layout, "softmax_scale": w.softmax_scale},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(achieved / peak, 4), "traffic": None,
+                     "frac": round(achieved / peak, 4), "traffic": measured_traffic(name, bwd=True),
                      "kernel": "attn_bwd_dq + attn_bwd_dkdv", "kernel_ms_avg": round(g["kernel_ms_avg"], 5),
                      "kernel_ms_median": round(g["kernel_ms_median"], 5), "flop_per_launch": flops,
                      "algorithmic_bytes_per_launch": nbytes,
