@@ -79,7 +79,8 @@ def test_kernel_hash_ignores_comments_only():
     assert bench.kernel_code(code) != bench.kernel_code(changed)
 
 
-@pytest.mark.parametrize("name", ["sdpa_b4h32n4096d128_bf16_causal", "fp8_b1h16n65536d128_causal_pv8"])
+@pytest.mark.parametrize("name", ["sdpa_b4h32n4096d128_bf16_causal", "fp8_b1h16n65536d128_causal",
+                                  "fp8_b1h16n65536d128_causal_pv8"])
 def test_traffic_records_are_well_formed(name):
     # a committed HBM-traffic record: keyed by a 16-hex source hash, and at
     # least the one-pass algorithmic bytes (a kernel cannot read less)
@@ -90,3 +91,21 @@ def test_traffic_records_are_well_formed(name):
     assert len(rec["kernel_sha256_16"]) == 16 and int(rec["kernel_sha256_16"], 16) >= 0
     w = WORKLOADS[name.replace("_pv8", "")]
     assert rec["hbm_bytes_per_launch"] >= bench.workload_bytes(w)
+
+
+def test_backward_traffic_record_is_well_formed():
+    # the backward's record: keyed by the backward sources' hash, and at least
+    # one pass over its algorithmic bytes (q, k, v, o, dout read; dq, dk, dv
+    # written; lse read and delta written)
+    import json
+    import os
+    name = "sdpa_b4h32n4096d128_bf16_causal"
+    with open(os.path.join(bench.ROOT, "profiles", f"traffic_bwd_{name}.json")) as f:
+        rec = json.load(f)
+    assert len(rec["kernel_sha256_16"]) == 16 and int(rec["kernel_sha256_16"], 16) >= 0
+    w = WORKLOADS[name]
+    q_el = w.batch * w.heads * w.seqlen * w.headdim
+    kv_el = w.batch * w.kv_heads * w.seqlen * w.headdim
+    alg = 2 * (3 * q_el + 2 * kv_el) + 2 * (q_el + 2 * kv_el) + 8 * w.batch * w.heads * w.seqlen
+    assert rec["hbm_bytes_per_launch"] >= alg
+    assert rec["hbm_bytes_per_launch"] == rec["hbm_read_bytes_per_launch"] + rec["hbm_write_bytes_per_launch"]
