@@ -649,6 +649,12 @@ attn_fwd_kernel(const FwdParams p) {
   const int t_lo = t_lo_key <= 0 ? 0 : (t_lo_key + kBN - 1) / kBN;
   const uint32_t t_span = (uint32_t)max(t_hi - t_lo, 0);
   auto tile_masked = [&](int kt) { return (uint32_t)(kt - t_lo) >= t_span; };
+  // keys [k0, k0 + 32) of half hb of tile kt seen by none of the wave's rows
+  auto half_dead = [&](int kt, int hb) {
+    const int k0 = kt * kBN + 32 * hb;
+    return k0 >= n || (p.causal && k0 > wr1 - 1) || (p.wr >= 0 && k0 > wr1 - 1 + p.wr) ||
+           (p.wl >= 0 && k0 + 31 < wr0 - p.wl);
+  };
 
   // ---- one 32-key half ("unit") of the software pipeline.  The softmax of
   // the current scores `sc` (tile kt, half hb) runs interleaved with the S
@@ -914,8 +920,11 @@ attn_fwd_kernel(const FwdParams p) {
         unit8(BoolTag<false>{}, s_b, 1, kbuf0, s_b, pb, [](int) {});
         tile_pv8(s_a, s_b, pa, pb, l_tile, vlast);
       } else {
-        unit(BoolTag<false>{}, s_a, 0, vlast, kbuf0, s_a, [](int) {});
-        unit(BoolTag<false>{}, s_b, 1, vlast, kbuf0, s_b, [](int) {});
+        // a half none of whose keys any of this wave's rows sees (past the
+        // causal diagonal or a window edge, or past the sequence) adds
+        // exactly nothing (p = 0): its softmax and P.V are skipped
+        if (!half_dead(kt, 0)) unit(BoolTag<false>{}, s_a, 0, vlast, kbuf0, s_a, [](int) {});
+        if (!half_dead(kt, 1)) unit(BoolTag<false>{}, s_b, 1, vlast, kbuf0, s_b, [](int) {});
       }
     }
     __syncthreads();   // the slots are reused by a second pass
