@@ -159,14 +159,18 @@ attn_bwd_dq_kernel(const BwdParams p) {
   const int col = lane & 31;
   const int n = p.n;
 
-  // heaviest query tiles first; query heads sharing a K/V head on one XCD
-  // (workgroup w runs on XCD w % 8), else groups of heads per XCD
+  // heaviest query tiles first, a few heads at a time per XCD (workgroup w
+  // runs on XCD w % 8): with shared K/V heads, the query heads of two K/V
+  // heads (one if the K/V heads only split into eights), the unit being
+  // (query tile, query head of the group); else groups of heads
   const int bh_count = p.batch * p.heads;
+  const int bhk_count = bh_count / p.group;
   int tile = p.q_tiles - 1 - (int)(blockIdx.x / bh_count);
   int bh = (int)(blockIdx.x % bh_count);
-  if (p.group > 1 && bh_count % (8 * p.group) == 0) {
-    const int x = bh & 7, y = bh >> 3;
-    bh = ((y / p.group) * 8 + x) * p.group + y % p.group;
+  if (p.group > 1 && bhk_count % 8 == 0) {
+    const int2 wo = xcd_grouped((int)blockIdx.x, p.q_tiles * p.group, bhk_count % 16 == 0 ? 2 : 1);
+    tile = p.q_tiles - 1 - wo.x / p.group;
+    bh = wo.y * p.group + wo.x % p.group;
   } else if (p.group == 1) {
     const int2 wo = bwd_order((int)blockIdx.x, p.q_tiles, bh_count);
     tile = p.q_tiles - 1 - wo.x;

@@ -191,6 +191,14 @@ def test_bwd_head_groups_per_xcd(batch, heads, mask):
     check_bwd(batch, heads, heads, 300, 64, "f16", mask, "bshd", 4700 + batch)
 
 
+@pytest.mark.parametrize("batch", [1, 2, 3])
+def test_bwd_shared_kv_head_groups_per_xcd(batch):
+    # (batch, K/V head) counts of 8, 16 and 24 with four query heads each: the
+    # dQ kernel takes the query heads of one (8, 24) or two (16) K/V heads per
+    # XCD at a time, the dK/dV kernel groups of K/V heads
+    check_bwd(batch, 32, 8, 300, 64, "bf16", "causal", "bshd", 4800 + batch)
+
+
 def test_bwd_deterministic():
     g = torch.Generator(device="cuda").manual_seed(5)
     q, k, v, do = (torch.randn((2, 1000, 8, 128), device="cuda", generator=g).to(torch.bfloat16) for _ in range(4))
