@@ -8,7 +8,15 @@ Tolerances (derived in the design notes from the output formats):
     2e-3 bound is out of reach of any bf16-output kernel.
   * fp8 inputs (bf16 output): max |O_gpu - O_ref| <= 3e-2 against the oracle
     on the dequantised inputs.
-  * LSE: max |LSE_gpu - LSE_ref| <= 1e-3 for every dtype.
+  * LSE: |LSE_gpu - LSE_ref| <= 1e-3 for 16-bit inputs (fp32 sums, exp2 and
+    log2).  For fp8 inputs, per row i, 1e-3 + scale 2^-13 max_j sum_d
+    |q_id k_jd| over the keys j row i sees: the 8-bit matrix instruction sums
+    each group of 8 of its 64 products keeping about 16 bits below the
+    group's largest and truncating (measured on the instruction: 2^8 plus
+    63 products of 2^-9 gives 2^8 + 56 x 2^-9), so a score loses less than
+    7 x 2^-16 of each group's largest product, under 2^-13 of sum_d |q_d k_d|
+    in all, and the LSE, a softmax-weighted mean of the scores, at most the
+    largest such loss.
 """
 from __future__ import annotations
 
@@ -55,8 +63,22 @@ def run_gpu(inp: Inputs, *, causal=False, window=(-1, -1), scale=None, layout="b
     return o, lse
 
 
-def compare(o_gpu: np.ndarray, o_ref: np.ndarray, lse_gpu: np.ndarray, lse_ref: np.ndarray, kind: str, what=""):
-    """Assert the R10/R11 criteria; returns a dict of the measured errors."""
+def lse_bound_fp8(qf: np.ndarray, kf: np.ndarray, scale: float, causal: bool, window, rows=None) -> np.ndarray:
+    """Per-row LSE bound for fp8 inputs (module docstring): one head's
+    dequantised q [N, D] and its K/V head's k [N, D]; the rows listed (all by
+    default)."""
+    n = qf.shape[0]
+    rows = np.arange(n) if rows is None else np.asarray(rows)
+    a = np.abs(qf[rows]) @ np.abs(kf).T                      # sum_d |q_id k_jd|
+    vis = oracle.visible(rows[:, None], np.arange(kf.shape[0])[None, :], kf.shape[0], causal, window[0], window[1])
+    m = np.where(vis, a, 0.0).max(axis=1) if a.size else np.zeros(len(rows))
+    return TOL_LSE + scale * 2.0 ** -13 * m
+
+
+def compare(o_gpu: np.ndarray, o_ref: np.ndarray, lse_gpu: np.ndarray, lse_ref: np.ndarray, kind: str, what="",
+            lse_tol=None):
+    """Assert the R10/R11 criteria; returns a dict of the measured errors.
+    `lse_tol`: elementwise LSE bounds (fp8), else TOL_LSE."""
     assert o_gpu.shape == o_ref.shape, (o_gpu.shape, o_ref.shape)
     assert np.isfinite(o_gpu).all(), f"{what}: non-finite output"
     err = np.abs(o_gpu - o_ref)
@@ -77,7 +99,12 @@ def compare(o_gpu: np.ndarray, o_ref: np.ndarray, lse_gpu: np.ndarray, lse_ref: 
         assert np.array_equal(np.isfinite(lse_gpu), fin), f"{what}: LSE finiteness differs"
         lerr = float(np.abs(lse_gpu[fin] - lse_ref[fin]).max()) if fin.any() else 0.0
         res["lse_max_abs"] = lerr
-        assert lerr <= TOL_LSE, f"{what}: max |dLSE| {lerr:.3g} > {TOL_LSE}"
+        if lse_tol is None:
+            assert lerr <= TOL_LSE, f"{what}: max |dLSE| {lerr:.3g} > {TOL_LSE}"
+        else:
+            tol = np.broadcast_to(lse_tol, lse_ref.shape)
+            excess = float((np.abs(lse_gpu[fin] - lse_ref[fin]) - tol[fin]).max()) if fin.any() else -1.0
+            assert excess <= 0, f"{what}: |dLSE| exceeds its fp8 bound by {excess:.3g} (max |dLSE| {lerr:.3g})"
     return res
 
 
@@ -94,7 +121,15 @@ def full_check(inp: Inputs, dtype: str, *, causal=False, window=(-1, -1), scale=
     D = qf.shape[-1]
     sc = 1.0 / math.sqrt(D) if scale is None else scale
     o_ref, lse_ref = oracle.attention(qf, kf, vf, scale=sc, causal=causal, window=window, layout=layout)
-    return compare(o.float().cpu().double().numpy(), o_ref, lse.cpu().double().numpy(), lse_ref, kind_of(dtype), what)
+    lse_tol = None
+    if dtype == "fp8":
+        qb = qf if layout == "bhsd" else np.swapaxes(qf, 1, 2)
+        kb = kf if layout == "bhsd" else np.swapaxes(kf, 1, 2)
+        B, H = qb.shape[0], qb.shape[1]
+        lse_tol = np.stack([np.stack([lse_bound_fp8(qb[b, h], kb[b, oracle.kv_head_of(h, H, kb.shape[1])], sc, causal,
+                                                    window) for h in range(H)]) for b in range(B)])
+    return compare(o.float().cpu().double().numpy(), o_ref, lse.cpu().double().numpy(), lse_ref, kind_of(dtype), what,
+                   lse_tol=lse_tol)
 
 
 def sampled_check(inp: Inputs, dtype: str, o_gpu: torch.Tensor, lse_gpu: torch.Tensor, heads, rows, *,
@@ -114,7 +149,7 @@ def sampled_check(inp: Inputs, dtype: str, o_gpu: torch.Tensor, lse_gpu: torch.T
         return stored_f64(x.contiguous(), s)
     hax = 2 if layout == "bshd" else 1
     hq, hk = inp.q.shape[hax], inp.k.shape[hax]
-    o_refs, l_refs = [], []
+    o_refs, l_refs, l_tols = [], [], []
     for (b, h) in heads:
         g = oracle.kv_head_of(h, hq, hk)   # the K/V head query head h reads
         qf = head_arr(inp.q, inp.descale[0], b, h)
@@ -124,7 +159,10 @@ def sampled_check(inp: Inputs, dtype: str, o_gpu: torch.Tensor, lse_gpu: torch.T
         o1, l1 = oracle.attention_head(qf, kf, vf, sc, causal, window[0], window[1], rows=rows)
         o_refs.append(o1)
         l_refs.append(l1)
-    return compare(np.stack(sel_o), np.stack(o_refs), np.stack(sel_l), np.stack(l_refs), kind_of(dtype), what)
+        if dtype == "fp8":
+            l_tols.append(lse_bound_fp8(qf, kf, sc, causal, window, rows=rows))
+    return compare(np.stack(sel_o), np.stack(o_refs), np.stack(sel_l), np.stack(l_refs), kind_of(dtype), what,
+                   lse_tol=np.stack(l_tols) if l_tols else None)
 
 
 def sample_rows(n: int, seed: int, extra: int = 96):

@@ -109,3 +109,20 @@ def test_sink_key_shared_by_every_row(dtype):
     v[0, 0] = 4.0
     v[0, 1] = -4.0
     full_check(_stored(q, k, v, dtype), dtype, causal=True, what=f"sink keys {dtype}")
+
+
+@pytest.mark.parametrize("pv8", [False, True])
+@pytest.mark.parametrize("factor", [16.0, 64.0, 256.0])
+@pytest.mark.parametrize("shape", [(2, 4, 4, 700, True, (-1, -1)), (1, 8, 2, 1000, False, (300, 40))])
+def test_fp8_scores_with_large_scales(shape, factor, pv8):
+    # fp8 inputs with the softmax scale 16-256 times 1/sqrt(d): very peaked
+    # rows (at 256 the fixed reference overflows and the exact-maximum pass
+    # runs), both formats of P; O within 3e-2, the LSE within the fp8 bound
+    # that includes the 8-bit matrix instruction's truncated group sums
+    # (parity_helpers)
+    import math
+    from exact_attention_04_amd.workloads import small_case
+    batch, heads, heads_kv, n, causal, window = shape
+    inp = small_case(batch, heads, n, 128, "fp8", "bshd", 6100 + int(factor) + (1 if pv8 else 0), heads_kv=heads_kv)
+    full_check(inp, "fp8", causal=causal, window=window, scale=factor / math.sqrt(128),
+               pv_dtype=torch.float8_e4m3fn if pv8 else None, what=f"fp8 x{factor} pv8={pv8} {shape}")
