@@ -180,7 +180,11 @@ def time_gpu_bwd(w, steps: int, warmup: int):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     kern_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    return {"ms_per_step": (t1 - t0) * 1e3 / steps, "kernel_ms_avg": float(np.mean(kern_ms)),
+
+    def run_once():
+        attention_backward(q, k, v, o, do, lse, dq=dq, dk=dk, dv=dv, delta=delta, **kw)
+
+    return {"run": run_once, "ms_per_step": (t1 - t0) * 1e3 / steps, "kernel_ms_avg": float(np.mean(kern_ms)),
             "kernel_ms_median": float(np.median(kern_ms)), "kernel_ms_min": float(np.min(kern_ms))}
 
 
@@ -513,6 +517,8 @@ def main_bwd(args, name, w):
                      "algorithmic_GBps": round(nbytes / (g["kernel_ms_avg"] * 1e-3) / 1e9, 1)},
         "cpu_baseline": None,
     }
+    if not args.no_clock:
+        rec["clock"] = sample_clock(g["run"], g["kernel_ms_median"])
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline_bwd(w, target_s=args.cpu_seconds)
     print(json.dumps(rec), flush=True)
