@@ -310,8 +310,9 @@ attn_bwd_dq_kernel(const BwdParams p) {
   //      come after step kLag)
   //   4. dQ^T += K_b^T dS_b^T, after the rest of half b's dS
   // Row fragments are read two steps ahead of their MFMAs, K^T fragments one
-  // MFMA ahead.  Each step is fenced so the compiler keeps this order.
-  auto step = [&](int kt, const unsigned char* kc, const unsigned char* vc) {
+  // MFMA ahead; `hook(st)` (the next tile's loads) runs after phase-1 step
+  // st.  Each step is fenced so the compiler keeps this order.
+  auto step = [&](int kt, const unsigned char* kc, const unsigned char* vc, auto&& hook) {
     const bool masked = (uint32_t)(kt - t_lo) >= t_span;
     f32x16 sa, dpa, sb, dpb;
 #pragma unroll
@@ -336,6 +337,7 @@ attn_bwd_dq_kernel(const BwdParams p) {
       read_rows(st + 2, rk[st & 1], rv[st & 1]);
       sa = mfma_16bit<IN>(ck, qf[st], sa);
       dpa = mfma_16bit<IN>(cv, df[st], dpa);
+      hook(st);
       __builtin_amdgcn_sched_barrier(0);
     }
     // 2
@@ -380,17 +382,44 @@ attn_bwd_dq_kernel(const BwdParams p) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     int kt = kt_begin;
+    // The next tile's loads go out one or two per phase-1 step (its kDma K
+    // blocks, then its kDma V blocks) rather than all before the step:
+    // issued together right after the barrier, the four waves' loads queue
+    // on the address unit (measured: the dQ kernel 2.4% faster spread).
+    constexpr int kPer = (2 * C::kDma + kS - 1) / kS;
+    auto dma_block = [&](const Rows64& rk, const Rows64& rv, unsigned char* kdst, unsigned char* vdst, int i) {
+      if (i < C::kDma) load_16b_to_lds(rk.base, rk.bytes, k_off[i], kdst + (wave * C::kDma + i) * 1024);
+      else if (i < 2 * C::kDma)
+        load_16b_to_lds(rv.base, rv.bytes, v_off[i - C::kDma], vdst + (wave * C::kDma + i - C::kDma) * 1024);
+    };
+    auto none = [](int) {};
     for (; kt + 1 < kt_end; kt += 2) {
-      issue(kt + 1, kbuf1, vbuf1);
-      step(kt, kbuf0, vbuf0);
+      {
+        const Rows64 rk = rows64(kg, k_stride, C::kRow, (kt + 1) * kBN, n);
+        const Rows64 rv = rows64(vg, v_stride, C::kRow, (kt + 1) * kBN, n);
+        step(kt, kbuf0, vbuf0, [&](int st) {
+#pragma unroll
+          for (int u = 0; u < kPer; ++u) dma_block(rk, rv, kbuf1, vbuf1, st * kPer + u);
+        });
+      }
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      if (kt + 2 < kt_end) issue(kt + 2, kbuf0, vbuf0);
-      step(kt + 1, kbuf1, vbuf1);
+      {
+        const bool more = kt + 2 < kt_end;
+        const int kn = more ? kt + 2 : kt + 1;   // (a tile inside the range either way)
+        const Rows64 rk = rows64(kg, k_stride, C::kRow, kn * kBN, n);
+        const Rows64 rv = rows64(vg, v_stride, C::kRow, kn * kBN, n);
+        step(kt + 1, kbuf1, vbuf1, [&](int st) {
+          if (more) {
+#pragma unroll
+            for (int u = 0; u < kPer; ++u) dma_block(rk, rv, kbuf0, vbuf0, st * kPer + u);
+          }
+        });
+      }
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     }
-    if (kt < kt_end) step(kt, kbuf0, vbuf0);
+    if (kt < kt_end) step(kt, kbuf0, vbuf0, none);
   }
 
   if (ok) {
