@@ -382,7 +382,7 @@ attn_bwd_dq_kernel(const BwdParams p) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     int kt = kt_begin;
-    // The next tile's loads go out one or two per phase-1 step (its kDma K
+    // The next tile's loads go out one per phase-1 step (its kDma K
     // blocks, then its kDma V blocks) rather than all before the step:
     // issued together right after the barrier, the four waves' loads queue
     // on the address unit (measured: the dQ kernel 2.4% faster spread).
